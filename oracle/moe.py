@@ -295,28 +295,38 @@ def moe_layer_tokens(wl, tokens, expert_cache=None) -> dict:
 
 # ----------------------------------------------------------- pre-routed groups
 
-def grouped_ffn(wl, rows_per_group=None, group_sample=None) -> dict:
+def grouped_ffn(wl, group_sample=None) -> dict:
     """Pre-routed grouped FFN (no routing, no combine): each routed group g
     runs expert g on its contiguous rows, the shared expert on the last
-    segment; outputs are bf16, unweighted.  `group_sample` maps a group index
-    (or 'shared') to the row indices within that group to evaluate."""
-    tbl = _E4M3_TABLE
+    segment; outputs unweighted, rounded to wl.out_dt.  `group_sample` maps a
+    group index (or 'shared') to the row indices within that group to
+    evaluate (all rows when absent).  Returns {group: (rows, y)}."""
     H = wl.H
-    qa = wl.a_q.cpu().numpy()
-    sa = wl.a_s.cpu().numpy().astype(np.float64)
     G = len(wl.group_m)
-    starts = np.concatenate([[0], np.cumsum(wl.group_m)])
+    starts = np.concatenate([[0], np.cumsum(wl.group_m)]).astype(np.int64)
+    if wl.w_dt == "e4m3":
+        qa = wl.a_q.cpu().numpy()
+        sa = wl.a_s.cpu().numpy().astype(np.float64)
+
+        def rows_of(idx):
+            return (_E4M3_TABLE[qa[idx]].reshape(len(idx), H // 128, 128) * sa[idx][:, :, None]).reshape(len(idx), H)
+    else:
+        xa = wl.x.float().cpu().numpy()
+
+        def rows_of(idx):
+            return xa[idx].astype(np.float64)
     res = {}
     segs = [(g, starts[g], wl.group_m[g]) for g in range(G)]
     if wl.shared_m:
         segs.append(("shared", starts[G], wl.shared_m))
     for g, r0, m in segs:
-        sel = np.arange(m) if group_sample is None else np.asarray(group_sample[g])
-        rows = r0 + sel
-        a = (tbl[qa[rows]].reshape(len(rows), H // 128, 128) * sa[rows][:, :, None]).reshape(len(rows), H)
+        sel = np.arange(m) if (group_sample is None or g not in group_sample) else np.asarray(group_sample[g])
+        if len(sel) == 0:
+            res[g] = (sel, np.zeros((0, H)))
+            continue
         bank, e = (wl.shared, 0) if g == "shared" else (wl.routed, g)
-        y = expert_ffn(a, *bank_expert_f64(bank, e), "e4m3")
-        res[g] = (sel, round_to(y, "bf16"))
+        y = expert_ffn(rows_of(r0 + sel), *bank_expert_f64(bank, e), h_mode_for(wl.w_dt))
+        res[g] = (sel, round_to(y, wl.out_dt))
     return res
 
 

@@ -1,0 +1,46 @@
+"""Algorithmic work of the grouped expert FFN: FLOPs and HBM bytes.
+
+FLOPs follow the pages' GEMM accounting ("DeepSeek V3/R1 Inference
+Efficiency (2)", section 2.3.1 and 2.4.1): "up & gate" is one
+[m, H] x [H, 2I] product (2 m H 2I FLOPs), "down" one [m, I] x [I, H] product
+(2 m I H), so one (row, expert) pair costs 6 H I FLOPs.
+
+Bytes count what the method must move at least once: the weights of every
+expert that has one or more rows (the experts no token chose are not read),
+their block scales, the activation rows read once, h written once and read
+once, and the expert outputs written once.
+"""
+from __future__ import annotations
+
+
+def gate_up_flops(m: int, H: int, I: int) -> int:
+    return 2 * m * H * 2 * I
+
+
+def down_flops(m: int, H: int, I: int) -> int:
+    return 2 * m * I * H
+
+
+def ffn_flops(rows: int, H: int, I: int) -> int:
+    return gate_up_flops(rows, H, I) + down_flops(rows, H, I)
+
+
+def weight_bytes_per_expert(H: int, I: int, w_dt: str) -> int:
+    eb = {"f32": 4, "bf16": 2, "e4m3": 1}[w_dt]
+    b = 3 * H * I * eb
+    if w_dt == "e4m3":
+        b += 3 * (H // 128) * (I // 128) * 4
+    return b
+
+
+def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w_dt: str, y_dt: str) -> int:
+    """Minimum HBM traffic of one grouped-FFN call.  group_rows: rows per
+    routed group (experts with 0 rows are not read)."""
+    eb = {"f32": 4, "bf16": 2, "e4m3": 1}
+    touched = sum(1 for m in group_rows if m > 0) + (1 if shared_rows > 0 else 0)
+    rows = sum(group_rows) + shared_rows
+    b = touched * weight_bytes_per_expert(H, I, w_dt)
+    a_row = H * eb[a_dt] + (H // 128 * 4 if a_dt == "e4m3" else 0)
+    h_row = I * eb[w_dt] + (I // 128 * 4 if w_dt == "e4m3" else 0)
+    b += rows * (a_row + 2 * h_row + H * eb[y_dt])
+    return b

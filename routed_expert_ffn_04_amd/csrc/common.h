@@ -1,0 +1,72 @@
+// Device helpers shared by the gfx950 kernels: number formats, wave64
+// primitives and MFMA operand types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// ---- bfloat16 (raw 16-bit patterns) ----------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even to bfloat16 (finite inputs): add 0x7FFF plus the
+// lowest kept bit, then truncate.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- OCP FP8 E4M3FN encode -------------------------------------------------
+// Round to nearest even, saturate the magnitude at 448 (code 0x7E), keep the
+// sign bit of the input.  Normal results (|v| >= 2^-6) round the fp32
+// significand at bit 20 (3 fraction bits kept); smaller magnitudes are
+// multiples of 2^-9 (subnormal codes 0..7, 8 meaning 2^-6).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fminf(fabsf(v), 448.0f);
+    const uint32_t ua = __float_as_uint(a);
+    const int ex = (int)(ua >> 23) - 127;
+    uint32_t code;
+    if (ex < -6) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);          // exact scaling, ties to even
+    } else {
+        const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);   // RNE at bit 20
+        code = ((((r >> 23) - 127u + 7u) & 0xFu) << 3) | ((r >> 20) & 7u);
+    }
+    return sign | code;
+}
+
+// ---- wave64 helpers ----------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, m, kWave);
+    hi = __shfl_xor(hi, m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Order-preserving map of an fp32 value to uint32 (for -0 == +0 callers must
+// canonicalise first).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace moe

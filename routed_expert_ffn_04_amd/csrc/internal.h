@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels (internal; the public C ABI is
+// include/moe.h).  Every launcher only enqueues on `stream` and returns the
+// hipError_t of the launch.  Arguments are validated by the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// route.hip
+hipError_t launch_router_logits(const void* x, int x_bf16, int T, int H, const float* wr,
+                                const float* bias, int E, float* logits, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int sigmoid,
+                              int32_t* ids, float* w, hipStream_t s);
+
+// permute.hip
+size_t permute_ws_bytes(int R, int E);
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* src, int32_t* dest, void* ws, hipStream_t s);
+
+// quant.hip
+hipError_t launch_quant_e4m3(const void* x, int x_bf16, int rows, int cols, uint8_t* q,
+                             float* scale, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y_perm, const void* y_sh, int y_bf16, const int32_t* dest,
+                          const float* w, int T, int k, int H, void* out, int out_bf16,
+                          hipStream_t s);
+
+// gffn.hip ------------------------------------------------------------------
+struct Bank {
+    const void* wg; const void* wu; const void* wd;
+    const float* sg; const float* su; const float* sd;
+};
+
+struct GffnProblem {
+    int dt;                       // 0 f32, 1 bf16, 2 e4m3 (activations and weights)
+    const void* a; const float* a_scale; const int32_t* src; int src_div;
+    const int32_t* offsets; int G; int R_max;
+    Bank routed;
+    const void* a_sh; const float* a_sh_scale; int S; int has_shared;
+    Bank shared;
+    int H, I;
+    void* y; void* y_sh; int y_bf16;
+};
+
+size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt);
+hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s);
+
+}  // namespace moe

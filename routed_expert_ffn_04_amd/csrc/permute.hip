@@ -1,0 +1,127 @@
+// Permute: expert histogram, exclusive scan and stable scatter of the T*k
+// token-expert assignments ("DeepSeek V3/R1 Inference Efficiency (2)",
+// section 2.3.1, operator "Expert: prepare routed GEMM").
+//
+// Integer-only and deterministic.  Stability (ascending flat index inside
+// each expert's segment) comes from ranking, never from atomics:
+//   1. per-chunk histograms (LDS integer atomics; only counts, order-free);
+//   2. one workgroup scans counts over experts and, per expert, over chunks:
+//      offsets, counts, and the base position of every (chunk, expert);
+//   3. each chunk ranks its items per expert with a wave64 multisplit
+//      (ballots on the id bits give the mask of lanes holding the same
+//      expert; rank = popcount of lower peers) plus the counts of the lower
+//      waves of the chunk, and scatters src/dest.
+// Sizes: chunk = 1024 items (16 waves); E <= 1024.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;
+constexpr int kChunkWaves = kChunk / kWave;
+
+static inline int nchunks(int R) { return (R + kChunk - 1) / kChunk; }
+
+size_t permute_ws_bytes(int R, int E) {
+    // chunk histograms / bases [nchunks][E] int32
+    return (size_t)nchunks(R) * E * sizeof(int32_t) + 256;
+}
+
+__global__ __launch_bounds__(kChunk) void perm_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                           int32_t* __restrict__ chunk_hist) {
+    __shared__ int32_t cnt[1024];
+    for (int e = threadIdx.x; e < E; e += kChunk) cnt[e] = 0;
+    __syncthreads();
+    const int f = blockIdx.x * kChunk + threadIdx.x;
+    if (f < R) {
+        const int e = ids[f];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // out-of-range ids are dropped
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kChunk) chunk_hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads; thread e owns expert e.  Turns chunk_hist
+// into chunk_base in place.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_hist, int nch, int E, int R,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int32_t c = 0;
+    if (e < E)
+        for (int ch = 0; ch < nch; ++ch) c += chunk_hist[(size_t)ch * E + e];
+    // exclusive scan of tot over e (1024 entries): wave scans + wave totals
+    const int lane = e % kWave, w = e / kWave;
+    int32_t v = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    if (lane == kWave - 1) wsum[w] = v;
+    __syncthreads();
+    int32_t wbase = 0;
+    for (int i = 0; i < w; ++i) wbase += wsum[i];
+    const int32_t excl = wbase + v - c;
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = excl;
+        int32_t run = excl;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int32_t h = chunk_hist[(size_t)ch * E + e];
+            chunk_hist[(size_t)ch * E + e] = run;
+            run += h;
+        }
+    }
+    if (e == 0) offsets[E] = R;
+}
+
+__global__ __launch_bounds__(kChunk) void perm_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                              int nbits, const int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ src, int32_t* __restrict__ dest) {
+    __shared__ int32_t wcnt[kChunkWaves][1024];   // items of expert e in wave w
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int f = blockIdx.x * kChunk + tid;
+    const int e0 = f < R ? ids[f] : -1;
+    const bool valid = (unsigned)e0 < (unsigned)E;        // out-of-range ids are dropped
+    const int e = valid ? e0 : 0;
+    // zero only the entries this chunk will read
+    for (int i = tid; i < kChunkWaves * E; i += kChunk) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+    // multisplit: lanes of this wave holding the same expert
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const uint64_t m = __ballot(valid && ((e >> b) & 1));
+        peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int rank = __popcll(peers & lower);
+    const bool leader = valid && ((peers & lower) == 0);
+    if (leader) wcnt[w][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+        int pos = chunk_base[(size_t)blockIdx.x * E + e] + rank;
+        for (int i = 0; i < w; ++i) pos += wcnt[i][e];
+        src[pos] = f;
+        dest[f] = pos;
+    }
+}
+
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* src, int32_t* dest, void* ws, hipStream_t s) {
+    const int nch = nchunks(R);
+    int32_t* chunk = (int32_t*)ws;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    if (nch > 0) {
+        hipLaunchKernelGGL(perm_hist_kernel, dim3(nch), dim3(kChunk), 0, s, ids, R, E, chunk);
+    }
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, chunk, nch, E, R, counts, offsets);
+    if (nch > 0) {
+        hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(kChunk), 0, s, ids, R, E, nbits, chunk, src, dest);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

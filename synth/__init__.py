@@ -289,18 +289,24 @@ def make_layer(T, H, E, k, I, *, x_dt="bf16", w_dt="bf16", out_dt="f32", score="
     return Workload(name, T, H, E, k, I, x_dt, w_dt, out_dt, score, x, wr, b, routed, sh)
 
 
-def make_grouped(group_m, shared_m, H, I, *, seed=4, device="cpu", w_std=0.02, name="custom-grouped") -> Workload:
-    """Pre-routed grouped input: len(group_m) routed experts plus one shared
-    expert, rows x ~ N(0,1) stored as e4m3 with per-1x128 fp32 scales."""
+def make_grouped(group_m, shared_m, H, I, *, dt="e4m3", seed=4, device="cpu", w_std=0.02,
+                 y_dt="bf16", name="custom-grouped") -> Workload:
+    """Pre-routed grouped input: len(group_m) routed experts (group g owns the
+    g-th contiguous run of rows) plus one shared expert on the last shared_m
+    rows; rows x ~ N(0,1).  dt 'e4m3': rows stored as e4m3 codes with
+    per-1x128 fp32 scales (a_q, a_s); 'bf16'/'f32': rows stored in x."""
     G = len(group_m)
     rows = sum(group_m) + shared_m
-    xa = normal((rows, H), seed, ST_X, 1.0, torch.float32, device)
-    a_q, a_s = block_quant_e4m3(xa, 1, 128)
-    del xa
-    routed = _bank(G, H, I, "e4m3", seed, (ST_RG, ST_RU, ST_RD), w_std, device)
-    sh = _bank(1, H, I, "e4m3", seed, (ST_SG, ST_SU, ST_SD), w_std, device) if shared_m > 0 else None
-    wl = Workload(name, 0, H, G, 8, I, "e4m3", "e4m3", "bf16", "none", routed=routed, shared=sh,
-                  group_m=list(group_m), shared_m=shared_m, a_q=a_q, a_s=a_s)
+    routed = _bank(G, H, I, dt, seed, (ST_RG, ST_RU, ST_RD), w_std, device)
+    sh = _bank(1, H, I, dt, seed, (ST_SG, ST_SU, ST_SD), w_std, device) if shared_m > 0 else None
+    wl = Workload(name, 0, H, G, 8, I, dt, dt, y_dt, "none", routed=routed, shared=sh,
+                  group_m=list(group_m), shared_m=shared_m)
+    if dt == "e4m3":
+        xa = normal((rows, H), seed, ST_X, 1.0, torch.float32, device)
+        wl.a_q, wl.a_s = block_quant_e4m3(xa, 1, 128)
+        del xa
+    else:
+        wl.x = normal((rows, H), seed, ST_X, 1.0, torch.float32 if dt == "f32" else torch.bfloat16, device)
     return wl
 
 
