@@ -1,0 +1,262 @@
+"""Benchmark of the MI355X sparse MoE FFN layer (one GPU).
+
+One step = one pass of the whole hot path over one batch of synthetic tokens:
+route -> (fp8 layers: quantise x) -> permute -> grouped FFN -> combine, each
+through the library's C ABI on torch's current stream (the same kernels
+moe_layer enqueues).  Inputs are resident in HBM before the timed region.
+HIP events around each call inside the timed region give per-call times; the
+grouped FFN (tile builder + gate/up kernel + down kernel) is the dominant call
+and its roofline fraction is reported against the MI355X peaks.
+
+Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped decode batch
+(T = 128, H = 7168, 256 routed experts + 1 shared, I = 2048, top-8, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import routed_expert_ffn_04_amd as moe  # noqa: E402
+from routed_expert_ffn_04_amd import accounting  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "MoE layer tokens/s at 1 GPU; grouped-FFN HBM GB/s (T=128) and MFMA TFLOPS (T=16384)"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_inputs(cid: int, dev):
+    t0 = time.time()
+    wl = synth.config(cid, device=dev)
+    torch.cuda.synchronize()
+    log(f"config {cid} ({wl.name}) generated on {dev} in {time.time() - t0:.1f}s")
+    return wl
+
+
+class LayerRunner:
+    """The layer as its five C-ABI calls with preallocated buffers."""
+
+    def __init__(self, wl, dev):
+        self.wl = wl
+        T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
+        self.routed = moe.Experts.from_bank(wl.routed)
+        self.shared = moe.Experts.from_bank(wl.shared) if wl.shared is not None else None
+        self.fp8 = wl.w_dt == "e4m3"
+        ydt = torch.bfloat16 if wl.out_dt == "bf16" else torch.float32
+        R = T * k
+        L = moe.lib()
+        self.ws_route = moe._workspace(L.moe_route_workspace_size(T, E), dev)
+        self.ws_perm = moe._workspace(L.moe_permute_workspace_size(T, k, E), dev)
+        rs = self.routed.struct()
+        self.ws_ffn = moe._workspace(L.moe_grouped_ffn_workspace_size(R, E, T if self.shared else 0, H, I, rs.dt), dev)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.src = torch.empty(R, dtype=torch.int32, device=dev)
+        self.dest = torch.empty(R, dtype=torch.int32, device=dev)
+        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.fp8 else None
+        self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.y = torch.empty((R, H), dtype=ydt, device=dev)
+        self.y_sh = torch.empty((T, H), dtype=ydt, device=dev) if self.shared else None
+        self.out = torch.empty((T, H), dtype=ydt, device=dev)
+        self.names = ["route", "quant", "permute", "grouped_ffn", "combine"] if self.fp8 else \
+            ["route", "permute", "grouped_ffn", "combine"]
+
+    def calls(self):
+        wl = self.wl
+        yield "route", lambda: moe.route(wl.x, wl.w_router, wl.bias, wl.k, wl.score, ws=self.ws_route,
+                                         out=(self.ids, self.w))
+        if self.fp8:
+            yield "quant", lambda: moe.quant_e4m3_1x128(wl.x, out=(self.xq, self.xs))
+        yield "permute", lambda: moe.permute(self.ids, wl.E, ws=self.ws_perm,
+                                             out=(self.counts, self.offsets, self.src, self.dest))
+        a, a_s = (self.xq, self.xs) if self.fp8 else (wl.x, None)
+        yield "grouped_ffn", lambda: moe.grouped_ffn(
+            a, self.offsets, self.routed, a_scale=a_s, src=self.src, src_div=wl.k, R_max=wl.T * wl.k,
+            a_sh=a if self.shared else None, a_sh_scale=a_s if self.shared else None, shared=self.shared,
+            y=self.y, y_sh=self.y_sh, ws=self.ws_ffn)
+        yield "combine", lambda: moe.combine(self.y, self.y_sh, self.dest, self.w, out=self.out)
+
+
+class GroupedRunner:
+    """The pre-routed expert-parallel share: the grouped FFN call alone."""
+
+    def __init__(self, wl, dev):
+        self.wl = wl
+        gm = wl.group_m
+        self.R = sum(gm)
+        self.offsets = torch.tensor([0] + list(torch.tensor(gm).cumsum(0).tolist()), dtype=torch.int32, device=dev)
+        self.routed = moe.Experts.from_bank(wl.routed)
+        self.shared = moe.Experts.from_bank(wl.shared) if wl.shared is not None else None
+        L = moe.lib()
+        rs = self.routed.struct()
+        self.ws = moe._workspace(L.moe_grouped_ffn_workspace_size(self.R, len(gm), wl.shared_m, wl.H, wl.I, rs.dt), dev)
+        self.y = torch.empty((self.R, wl.H), dtype=torch.bfloat16, device=dev)
+        self.y_sh = torch.empty((wl.shared_m, wl.H), dtype=torch.bfloat16, device=dev)
+        self.names = ["grouped_ffn"]
+
+    def calls(self):
+        wl, R = self.wl, self.R
+        yield "grouped_ffn", lambda: moe.grouped_ffn(
+            wl.a_q, self.offsets, self.routed, a_scale=wl.a_s, R_max=R, a_sh=wl.a_q[R:], a_sh_scale=wl.a_s[R:],
+            shared=self.shared, y=self.y, y_sh=self.y_sh, ws=self.ws)
+
+
+def run_timed(runner, steps: int, warmup: int):
+    for _ in range(warmup):
+        for _, f in runner.calls():
+            f()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        row = []
+        for name, f in runner.calls():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            row.append((name, e0, e1))
+        evs.append(row)
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per = {}
+    for row in evs:
+        for name, e0, e1 in row:
+            per.setdefault(name, []).append(e0.elapsed_time(e1))
+    return total_ms / steps, {k: sum(v) / len(v) for k, v in per.items()}, wall
+
+
+def cpu_baseline(wl, cid: int, sample_tokens: int):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload
+    (the oracle copies to the host only the experts its sample touches)."""
+    import copy
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle import moe as om
+    oracle.build(force=False)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        if cid == 4:
+            gs = {g: list(range(min(sample_tokens, wl.group_m[g]))) for g in range(len(wl.group_m))}
+            gs["shared"] = list(range(min(sample_tokens, wl.shared_m)))
+            om.grouped_ffn(wl, group_sample=gs)
+            n = sum(len(v) for v in gs.values())
+            sample = f"first {sample_tokens} rows of each of the {len(gs)} groups"
+        elif sample_tokens >= wl.T:
+            om.moe_layer(wl)
+            n = wl.T
+            sample = f"whole workload ({wl.T} tokens)"
+        else:
+            sub = copy.copy(wl)
+            sub.x = wl.x[:sample_tokens]
+            sub.T = sample_tokens
+            om.moe_layer_tokens(sub, list(range(sample_tokens)))
+            n = sample_tokens
+            sample = f"first {sample_tokens} of {wl.T} tokens (each token routed and run through its experts)"
+        dt = time.perf_counter() - t0
+    unit = "rows/s" if cid == 4 else "tokens/s"
+    return {"value": round(n / dt, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the T=128 decode batch)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="tokens (rows) in the CPU oracle sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    cid = args.config
+    wl = build_inputs(cid, dev)
+    runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev)
+    ms, per, wall = run_timed(runner, args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; per call (ms): " +
+        ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+
+    # algorithmic work of the grouped FFN
+    if cid == 4:
+        group_rows = list(wl.group_m)
+        shared_rows = wl.shared_m
+        a_dt, y_dt = "e4m3", "bf16"
+    else:
+        group_rows = runner.counts.cpu().tolist()
+        shared_rows = wl.T if wl.shared is not None else 0
+        a_dt = "e4m3" if wl.w_dt == "e4m3" else wl.x_dt
+        y_dt = wl.out_dt
+    rows = sum(group_rows) + shared_rows
+    flops = accounting.ffn_flops(rows, wl.H, wl.I)
+    nbytes = accounting.grouped_ffn_bytes(group_rows, shared_rows, wl.H, wl.I, a_dt, wl.w_dt, y_dt)
+    gffn_ms = per["grouped_ffn"]
+    gbs = nbytes / (gffn_ms * 1e-3) / 1e9
+    tfs = flops / (gffn_ms * 1e-3) / 1e12
+    mem_bound = nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_TFLOPS[wl.w_dt] * 1e12)
+    if mem_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_TFLOPS[wl.w_dt], "unit": "TFLOP/s",
+                "frac": round(tfs / PEAK_TFLOPS[wl.w_dt], 4), "traffic": None}
+    roof["kernel"] = "moe_grouped_ffn (tile list + gate/up + down kernels)"
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["kernel_ms"] = round(gffn_ms, 4)
+
+    if cid == 4:
+        value, unit = rows / (ms * 1e-3), "rows/s"
+    else:
+        value, unit = wl.T / (ms * 1e-3), "tokens/s"
+    cfg = {"workload": wl.name, "H": wl.H, "I": wl.I, "weights": wl.w_dt}
+    if cid == 4:
+        cfg.update(groups=len(wl.group_m), group_rows=list(wl.group_m), shared_rows=wl.shared_m)
+    else:
+        cfg.update(T=wl.T, E=wl.E, k=wl.k, shared=int(wl.shared is not None), score=wl.score,
+                   bias="zipf1.2" if wl.bias is not None else None, x=wl.x_dt, out=wl.out_dt,
+                   experts_touched=sum(1 for c in group_rows if c > 0))
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "e4m3": "fp8-e4m3", "f32": "f32"}[wl.w_dt],
+        "data": "synthetic (seeded counter-based normals; random-init weights)", "config": cfg,
+        "roofline": roof,
+        "grouped_ffn": {"ms": round(gffn_ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)},
+        "calls_ms": {k: round(v, 4) for k, v in per.items()},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle baseline ...")
+        res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 1 else 64)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -141,13 +141,16 @@ class Experts:
 
 # ---------------------------------------------------------------- entry points
 
-def route(x, w_router, bias, k: int, score: str, stream=None, ws=None):
+def route(x, w_router, bias, k: int, score: str, stream=None, ws=None, out=None):
     """topk_ids [T][k] int32, topk_w [T][k] fp32 (moe_route)."""
     import torch
     T, H = x.shape
     E = w_router.shape[1]
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    else:
+        ids, w = out
     need = lib().moe_route_workspace_size(T, E)
     ws = ws if ws is not None else _workspace(need, x.device)
     _check(lib().moe_route(_ptr(x), _dt_of(x), T, H, _ptr(w_router), _ptr(bias), E, k, SCORE[score],
@@ -155,15 +158,18 @@ def route(x, w_router, bias, k: int, score: str, stream=None, ws=None):
     return ids, w
 
 
-def permute(topk_ids, E: int, stream=None, ws=None):
+def permute(topk_ids, E: int, stream=None, ws=None, out=None):
     """counts [E], offsets [E+1], src [T*k], dest [T*k] (moe_permute)."""
     import torch
     T, k = topk_ids.shape
     dev = topk_ids.device
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    src = torch.empty(T * k, dtype=torch.int32, device=dev)
-    dest = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if out is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(T * k, dtype=torch.int32, device=dev)
+        dest = torch.empty(T * k, dtype=torch.int32, device=dev)
+    else:
+        counts, offsets, src, dest = out
     need = lib().moe_permute_workspace_size(T, k, E)
     ws = ws if ws is not None else _workspace(need, dev)
     _check(lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(src), _ptr(dest),
@@ -171,12 +177,15 @@ def permute(topk_ids, E: int, stream=None, ws=None):
     return counts, offsets, src, dest
 
 
-def quant_e4m3_1x128(x, stream=None):
+def quant_e4m3_1x128(x, stream=None, out=None):
     """codes [rows][cols] uint8, scales [rows][cols/128] fp32."""
     import torch
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    if out is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
     _check(lib().moe_quant_e4m3_1x128(_ptr(x), _dt_of(x), rows, cols, _ptr(q), _ptr(s), _stream(stream)))
     return q, s
 
