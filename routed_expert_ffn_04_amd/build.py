@@ -12,9 +12,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
+PROBE = os.path.join(HERE, "moe_probe")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "permute.hip", "quant.hip", "combine.hip", "gffn.hip", "api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "quant.hip", "combine.hip", "gffn.hip", "gffn_tile.hip",
+           "gffn_stream.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -26,28 +29,38 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, extra=(), build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link lib_path (extra_flags: additional hipcc
+    flags, e.g. -D tuning macros for experiments built elsewhere)."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, tuple(extra_flags), build_dir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
+    if lib_path == LIB:
+        # native driver of the C ABI (counter runs without Python)
+        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, os.path.join(CSRC, "moe_probe.cpp"), "-o", PROBE + ".tmp",
+               "-L", HERE, "-lmoe_gfx950", "-Wl,-rpath,$ORIGIN"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"moe_probe build failed:\n{r.stderr}")
+        os.replace(PROBE + ".tmp", PROBE)
     if verbose:
-        print(LIB)
-    return LIB
+        print(lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -1,7 +1,7 @@
 // C ABI of the sparse MoE FFN layer (declarations and contracts: include/moe.h).
 // Validation, workspace carving and kernel launches; no allocation, no
 // host synchronisation.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 

@@ -1,0 +1,117 @@
+// Shared definitions of the grouped expert FFN kernels: arguments, MFMA
+// operand traits, group lookup, and the persistent work queues.
+#pragma once
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+template <int DT> struct Op;
+template <> struct Op<DT_F32> {
+    static constexpr int EB = 4;      // bytes per element
+    static constexpr int KI = 4;      // k per MFMA
+    static constexpr int LB = 4;      // bytes per lane per MFMA operand
+    __device__ static f32x4 mma(const uint8_t* a, const uint8_t* b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(*(const float*)a, *(const float*)b, c, 0, 0, 0);
+    }
+};
+template <> struct Op<DT_BF16> {
+    static constexpr int EB = 2, KI = 32, LB = 16;
+    __device__ static f32x4 mma(const uint8_t* a, const uint8_t* b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)a, *(const bf16x8*)b, c, 0, 0, 0);
+    }
+};
+template <> struct Op<DT_E4M3> {
+    static constexpr int EB = 1, KI = 128, LB = 32;
+    __device__ static f32x4 mma(const uint8_t* a, const uint8_t* b, f32x4 c) {
+        const i32x4 a0 = *(const i32x4*)a, a1 = *(const i32x4*)(a + 16);
+        const i32x4 b0 = *(const i32x4*)b, b1 = *(const i32x4*)(b + 16);
+        const i32x8 av = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const i32x8 bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        // operand formats 0/0 = FP8 E4M3; e8m0 scales 127 = 1.0
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+
+constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kClasses = 3;       // tile classes by rows per group
+
+// A work list of m-tiles (group, first row) for one tile class, written by
+// the list builder; the tiles of a launch are (entry, n-tile) pairs.
+struct TileList {
+    const int2* entries;
+    const int* count;           // number of entries
+};
+
+struct GArgs {
+    const uint8_t* a; const float* a_scale; const int32_t* src; int src_div;
+    const uint8_t* a_sh; const float* a_sh_scale;
+    const int32_t* offsets; int G; int R_max; int S;
+    Bank routed, shared;
+    int H, I;
+    uint8_t* h; float* h_scale;        // [R_max + S][I], [R_max + S][I/128]
+    void* y; void* y_sh; int y_bf16;
+};
+
+struct GroupInfo {
+    int p0, m, e, shared;
+};
+
+__device__ __forceinline__ GroupInfo group_info(const GArgs& A, int g) {
+    GroupInfo gi;
+    if (g < A.G) {
+        gi.p0 = min(max(A.offsets[g], 0), A.R_max);
+        gi.m = min(max(A.offsets[g + 1] - gi.p0, 0), A.R_max - gi.p0);
+        gi.e = g;
+        gi.shared = 0;
+    } else {
+        gi.p0 = 0;
+        gi.m = A.S;
+        gi.e = 0;
+        gi.shared = 1;
+    }
+    return gi;
+}
+
+// Row index of tile row r in the h buffer (routed rows first, then shared).
+__device__ __forceinline__ int h_row(const GArgs& A, const GroupInfo& gi, int r) {
+    return gi.shared ? A.R_max + r : gi.p0 + r;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+// Static, die-aware assignment of the tiles of a list to a persistent grid.
+// Workgroups are dispatched to the kXcds dies round robin, so workgroup b runs
+// on die b % kXcds.  The tile range is cut into kXcds contiguous chunks and
+// the workgroups of die x stride through chunk x: consecutive tiles (the
+// n-tiles of one m-tile, which share activation rows) stay in one die's L2.
+// No atomics: every tile costs about the same within a class, and the list is
+// already in longest-first order.  Iterate with
+//   for (TileIter it(L, per_entry); it.valid(); it.next()) { ... it.t ... }
+struct TileIter {
+    long t, end, stride;
+    __device__ TileIter(const TileList& L, int per_entry) {
+        const long total = (long)(*L.count) * per_entry;
+        const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+        const int nwg_x = ((int)gridDim.x - x + kXcds - 1) / kXcds;
+        const long lo = total * x / kXcds;
+        end = total * (x + 1) / kXcds;
+        t = lo + j;
+        stride = nwg_x;
+    }
+    __device__ bool valid() const { return t < end; }
+    __device__ void next() { t += stride; }
+};
+
+// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip).
+hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
+hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
+hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_stream_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,184 @@
+// moe_probe: a native driver of the C ABI (no Python, no torch), used for
+// hardware-counter runs (rocprofv3 --pmc) and quick timing.
+//
+//   moe_probe decode  [iters]   T=128,   H=7168, 256+1 experts, I=2048, top-8, bf16, fp32 out
+//   moe_probe skew    [iters]   T=4096,  same layer, additive logit bias on 20 experts
+//   moe_probe prefill [iters]   T=16384, same layer with e4m3 block-scaled weights, bf16 out
+//   moe_probe copy    [iters]   a plain device copy of 1 GiB (counter calibration)
+//
+// Inputs are filled on the device from a hash of the element index (uniform
+// values with the layer's scales); values matter here only through the
+// routing distribution, which is close to uniform except for `skew`.
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+
+#define CK(x)                                                                         \
+    do {                                                                              \
+        hipError_t e_ = (x);                                                          \
+        if (e_ != hipSuccess) {                                                       \
+            fprintf(stderr, "%s:%d %s: %s\n", __FILE__, __LINE__, #x, hipGetErrorString(e_)); \
+            exit(2);                                                                  \
+        }                                                                             \
+    } while (0)
+
+#define CM(x)                                                                         \
+    do {                                                                              \
+        moe_status_t s_ = (x);                                                        \
+        if (s_ != MOE_OK) {                                                           \
+            fprintf(stderr, "%s: %s (%s)\n", #x, moe_status_string(s_), moe_last_error()); \
+            exit(3);                                                                  \
+        }                                                                             \
+    } while (0)
+
+__device__ __forceinline__ uint32_t hash32(uint64_t x) {
+    x ^= x >> 33;
+    x *= 0xff51afd7ed558ccdull;
+    x ^= x >> 33;
+    x *= 0xc4ceb9fe1a85ec53ull;
+    x ^= x >> 33;
+    return (uint32_t)x;
+}
+
+// uniform in [-a, a)
+__device__ __forceinline__ float uni(uint64_t seed, size_t i, float a) {
+    return ((float)hash32(seed * 0x9E3779B97F4A7C15ull + i) * (1.0f / 2147483648.0f) - 1.0f) * a;
+}
+
+__global__ void fill_f32(float* p, size_t n, uint64_t seed, float a) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = uni(seed, i, a);
+}
+
+__global__ void fill_bf16(uint16_t* p, size_t n, uint64_t seed, float a) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t u = __float_as_uint(uni(seed, i, a));
+        p[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+}
+
+// random finite e4m3 codes with magnitude exponent <= 2^3 (no NaN)
+__global__ void fill_e4m3(uint8_t* p, size_t n, uint64_t seed) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t h = hash32(seed * 0x9E3779B97F4A7C15ull + i);
+        p[i] = (uint8_t)((h & 0x80u) | (h % 0x50u));
+    }
+}
+
+__global__ void copy_u4(const uint4* __restrict__ s, uint4* __restrict__ d, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        d[i] = s[i];
+}
+
+static void* dalloc(size_t bytes) {
+    void* p = nullptr;
+    CK(hipMalloc(&p, bytes < 256 ? 256 : bytes));
+    return p;
+}
+
+struct BankBuf {
+    moe_experts_t d;
+};
+
+static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
+    BankBuf b{};
+    const size_t ne = (size_t)n * H * I;
+    const size_t eb = dt == MOE_E4M3 ? 1 : 2;
+    void* g = dalloc(ne * eb);
+    void* u = dalloc(ne * eb);
+    void* w = dalloc(ne * eb);
+    if (dt == MOE_E4M3) {
+        hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)g, ne, seed + 1);
+        hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)u, ne, seed + 2);
+        hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)w, ne, seed + 3);
+        const size_t ns = (size_t)n * (H / 128) * (I / 128);
+        float* sg = (float*)dalloc(ns * 4);
+        float* su = (float*)dalloc(ns * 4);
+        float* sd = (float*)dalloc(ns * 4);
+        for (float* s : {sg, su, sd}) hipLaunchKernelGGL(fill_f32, dim3(256), dim3(256), 0, 0, s, ns, seed + 7, 1e-3f);
+        b.d.s_gate = sg; b.d.s_up = su; b.d.s_down = sd;
+    } else {
+        const float a = 0.0346f;   // uniform with standard deviation 0.02
+        hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)g, ne, seed + 1, a);
+        hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)u, ne, seed + 2, a);
+        hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)w, ne, seed + 3, a);
+    }
+    b.d.n = n; b.d.H = H; b.d.I = I; b.d.dt = dt;
+    b.d.w_gate = g; b.d.w_up = u; b.d.w_down = w;
+    return b;
+}
+
+int main(int argc, char** argv) {
+    const std::string mode = argc > 1 ? argv[1] : "decode";
+    const int iters = argc > 2 ? atoi(argv[2]) : 5;
+    hipStream_t st;
+    CK(hipStreamCreate(&st));
+    hipEvent_t e0, e1;
+    CK(hipEventCreate(&e0));
+    CK(hipEventCreate(&e1));
+
+    if (mode == "copy") {
+        const size_t bytes = (size_t)1 << 30;
+        void* s = dalloc(bytes);
+        void* d = dalloc(bytes);
+        CK(hipMemsetAsync(s, 1, bytes, st));
+        const size_t n = bytes / 16;
+        hipLaunchKernelGGL(copy_u4, dim3(8192), dim3(256), 0, st, (const uint4*)s, (uint4*)d, n);
+        CK(hipEventRecord(e0, st));
+        for (int i = 0; i < iters; ++i)
+            hipLaunchKernelGGL(copy_u4, dim3(8192), dim3(256), 0, st, (const uint4*)s, (uint4*)d, n);
+        CK(hipEventRecord(e1, st));
+        CK(hipEventSynchronize(e1));
+        float ms = 0;
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        printf("copy 1 GiB: %.3f ms/iter, %.1f GB/s (read+write)\n", ms / iters, 2.0 * bytes / (ms / iters * 1e-3) / 1e9);
+        return 0;
+    }
+
+    int T, x_dt = MOE_BF16, w_dt, out_dt;
+    bool bias = false;
+    if (mode == "decode") { T = 128; w_dt = MOE_BF16; out_dt = MOE_F32; }
+    else if (mode == "skew") { T = 4096; w_dt = MOE_BF16; out_dt = MOE_F32; bias = true; }
+    else if (mode == "prefill") { T = 16384; w_dt = MOE_E4M3; out_dt = MOE_BF16; }
+    else { fprintf(stderr, "unknown mode %s\n", mode.c_str()); return 1; }
+    const int H = 7168, E = 256, k = 8, I = 2048;
+
+    void* x = dalloc((size_t)T * H * 2);
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)x, (size_t)T * H, 11, 1.73f);
+    float* wr = (float*)dalloc((size_t)H * E * 4);
+    hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, wr, (size_t)H * E, 12, 1.73f / 84.7f);
+    float* b = nullptr;
+    if (bias) {
+        std::vector<float> hb(E, -1.0f);
+        for (int e = 0; e < 20; ++e) hb[(e * 37) % E] = 2.5f;   // 20 hot experts
+        b = (float*)dalloc(E * 4);
+        CK(hipMemcpy(b, hb.data(), E * 4, hipMemcpyHostToDevice));
+    }
+    BankBuf routed = make_bank(E, H, I, w_dt, 100);
+    BankBuf shared = make_bank(1, H, I, w_dt, 200);
+    void* out = dalloc((size_t)T * H * (out_dt == MOE_BF16 ? 2 : 4));
+    const size_t wsb = moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, 1, out_dt);
+    void* ws = dalloc(wsb);
+    CK(hipDeviceSynchronize());
+
+    auto run = [&]() {
+        CM(moe_layer(x, x_dt, T, H, wr, b, E, k, MOE_SIGMOID, &routed.d, &shared.d, out, out_dt, nullptr,
+                     nullptr, nullptr, ws, wsb, st));
+    };
+    run();
+    CK(hipEventRecord(e0, st));
+    for (int i = 0; i < iters; ++i) run();
+    CK(hipEventRecord(e1, st));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    printf("%s: T=%d %.3f ms/layer, %.0f tokens/s\n", mode.c_str(), T, ms / iters, T / (ms / iters * 1e-3));
+    return 0;
+}
