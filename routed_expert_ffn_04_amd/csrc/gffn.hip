@@ -7,7 +7,8 @@
 // one of three tile classes by its row count m, read on the device:
 //   class 0: m <= 16          weight-streaming tiles of 16 rows   (bf16)
 //   class 1: 16 < m <= 256    weight-streaming tiles of 64 rows   (bf16)
-//   class 2: otherwise        LDS-tiled MFMA tiles of 64 rows     (any type)
+//   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
+//                             or 64-row LDS tiles (fp32 or H % 256 != 0)
 // (non-bf16 layers put every group in class 2).  One single-workgroup kernel
 // writes, per class, the list of (group, first row) m-tiles with the heaviest
 // groups first (longest-processing-time order); then each class's gate/up
@@ -133,16 +134,21 @@ int device_cu_count() {
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-static ClassSpec class_spec(int dt) {
+// Large groups use the 256 x 256 tiles of gffn_big.hip (bf16 / e4m3 with
+// H a multiple of 256), otherwise the 64-row LDS tiles of gffn_tile.hip.
+static bool use_big(int dt, int H) { return (dt == DT_BF16 || dt == DT_E4M3) && H % 256 == 0; }
+
+static ClassSpec class_spec(int dt, int H) {
     ClassSpec c{};
+    const int bm2 = use_big(dt, H) ? 256 : 64;
     if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
-        c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = 64;
+        c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
     } else {
         c.mlo[0] = 0;  c.mhi[0] = 0;        c.bm[0] = 16;   // unused
         c.mlo[1] = 0;  c.mhi[1] = 0;        c.bm[1] = 64;   // unused
-        c.mlo[2] = 0;  c.mhi[2] = 1 << 30;  c.bm[2] = 64;
+        c.mlo[2] = 0;  c.mhi[2] = 1 << 30;  c.bm[2] = bm2;
     }
     return c;
 }
@@ -160,10 +166,9 @@ static void max_entries(int R_max, int G, int S, const ClassSpec& c, int out[kCl
 }
 
 size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt) {
-    (void)H;
     const size_t rows = (size_t)R_max + S;
     const int eb = dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1;
-    const ClassSpec cs = class_spec(dt);
+    const ClassSpec cs = class_spec(dt, H);
     int me[kClasses];
     max_entries(R_max, G, S, cs, me);
     size_t b = align256(rows * I * eb);
@@ -182,7 +187,7 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     A.y = p.y; A.y_sh = p.y_sh; A.y_bf16 = p.y_bf16;
     const size_t rows = (size_t)p.R_max + A.S;
     const int eb = p.dt == DT_F32 ? 4 : p.dt == DT_BF16 ? 2 : 1;
-    const ClassSpec cs = class_spec(p.dt);
+    const ClassSpec cs = class_spec(p.dt, p.H);
     int me[kClasses];
     max_entries(p.R_max, p.G, A.S, cs, me);
 
@@ -209,11 +214,13 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     // phase 1 (all classes), then phase 2: a group's down tiles need all of its h
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
+        e = k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
+                  : use_big(p.dt, p.H) ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
+        e = k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
+                  : use_big(p.dt, p.H) ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
     }
     return e;
 }

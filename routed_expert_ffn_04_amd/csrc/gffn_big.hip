@@ -1,0 +1,338 @@
+// Grouped expert FFN, large tiles for groups with many rows (e4m3 and bf16).
+//
+// "DeepSeek V3/R1 Inference Efficiency (2)", section 2.3.1: at prefill sizes
+// the routed experts see thousands of rows each ("up & gate" [7168, 4096] and
+// "down" [2048, 7168] per group, FP8) and the GEMMs are compute-bound.
+//
+// Tile: 256 rows x 256 MFMA columns (gate/up: 128 gate + 128 up columns of
+// the same 128 h columns; down: 256 output columns), K staged 128 bytes at a
+// time in a double-buffered LDS ring fed by direct global->LDS 16-byte loads
+// (no VGPR round trip).  LDS rows are 128 bytes with the eight 16-byte chunks
+// XOR-swizzled by (row & 7) so that MFMA fragment reads spread over the banks.
+// 8 waves (2 along M x 4 along N), each computing 128 x 64 with 16x16 MFMA
+// blocks.
+//   e4m3: one v_mfma_scale_f32_16x16x128_f8f6f4 per block and stage covers a
+//         whole 128-wide scaling block; its partial is added to the fp32
+//         accumulator with one FMA by (activation scale x weight scale), the
+//         products being formed once per row and stage in LDS.
+//   bf16: two v_mfma_f32_16x16x32_bf16 per block and stage, no scaling.
+// The gate/up epilogue applies SwiGLU and quantises h per row and 128-column
+// block (e4m3) or rounds it (bf16); the down epilogue writes y.
+//
+// Tiles of a group are ordered n-tile-major with the group's m-tiles
+// innermost, so the m-tiles that share a weight tile run side by side on one
+// die (see TileIter) and the weight tile is read from HBM once.
+#include "gffn_common.h"
+
+namespace moe {
+
+constexpr int kBigM = 256;        // rows per tile
+constexpr int kBigN = 256;        // MFMA columns per tile
+constexpr int kStage = 128;       // K bytes per stage
+constexpr int kStageBytes = (kBigM + kBigN) * kStage;   // 64 KiB: A rows then B rows
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ (row & 7)) << 4); }
+
+// Issue the direct loads of one stage: 512 rows x 8 chunks = 4096 16-byte
+// chunks; every instruction of a wave fills 1 KiB of LDS = 8 rows.
+// arow[r] / brow[r]: row base pointers (already offset to k0 = 0).
+__device__ __forceinline__ void issue_stage(uint8_t* lds_stage, const uint8_t* const* rows, size_t k0, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int region = wave * 8 + q;               // 64 regions of 8 rows
+        const int row = region * 8 + lane / 8;         // 0 .. 511
+        const int pos = lane % 8;                      // chunk position in LDS
+        const int chunk = pos ^ (row & 7);             // chunk of the row stored there
+        const uint8_t* g = rows[row] + k0 + chunk * 16;
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds_stage + region * 1024), 16, 0, 0);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_frag(const uint8_t* base, int row, int lane, int step, i32x8& f8, bf16x8& f16) {
+    if (DT == DT_E4M3) {
+        const int c0 = 2 * (lane / 16);
+        const i32x4 lo = *(const i32x4*)(base + swz(row, c0));
+        const i32x4 hi = *(const i32x4*)(base + swz(row, c0 + 1));
+        f8 = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+        f16 = *(const bf16x8*)(base + swz(row, step * 4 + lane / 16));
+    }
+}
+
+// PHASE 0: gate/up (+SwiGLU epilogue); PHASE 1: down.
+template <int DT, int PHASE>
+__global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
+    constexpr bool FP8 = DT == DT_E4M3;
+    constexpr int EB = FP8 ? 1 : 2;
+    const int H = A.H, I = A.I;
+    const int K = PHASE == 0 ? H : I;                 // reduction length
+    const int NOUT = PHASE == 0 ? I : H;               // output columns of the phase
+    const int ncol = PHASE == 0 ? kBigN / 2 : kBigN;   // output columns per tile
+    const int ntn = NOUT / ncol;
+    const int nstages = K * EB / kStage;
+    const int nkb = K / 128;
+
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    uint8_t* stage_buf = smem;                                       // 2 x 64 KiB
+    const uint8_t** rows = (const uint8_t**)(smem + 2 * kStageBytes); // 512 row pointers
+    int* out_row = (int*)(rows + 512);                               // 256 output rows (-1: none)
+    const float** srow = (const float**)(out_row + kBigM);           // 256 activation-scale rows
+    float* sprod = (float*)(srow + kBigM);                           // [2 stages][2][256]
+    float* red = sprod + 2 * 2 * kBigM;                              // [4][256] amax partials
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+
+    for (TileIter it(L, ntn); it.valid(); it.next()) {
+        // ---- decode: tiles of a group are n-tile-major, m-tiles innermost
+        const int t = (int)it.t;
+        const int eidx = t / ntn;
+        const int2 ent = L.entries[eidx];
+        const GroupInfo gi = group_info(A, ent.x);
+        const int cg = (gi.m + kBigM - 1) / kBigM;
+        const int bg = eidx - ent.y / kBigM;
+        const int local = t - bg * ntn;
+        const int nt = local / cg, mt = local % cg;
+        const int m0 = mt * kBigM;
+        const int n0 = nt * ncol;
+        const int valid = min(gi.m - m0, kBigM);
+        const Bank& bk = gi.shared ? A.shared : A.routed;
+
+        __syncthreads();   // previous tile is done with LDS
+        if (tid < kBigM) {
+            const int r = min(m0 + tid, gi.m - 1);          // rows past the end re-read the last row
+            const uint8_t* p;
+            const float* ps = nullptr;
+            if (PHASE == 0) {
+                int ar;
+                const uint8_t* base;
+                const float* sbase;
+                if (gi.shared) {
+                    ar = r; base = A.a_sh; sbase = A.a_sh_scale;
+                } else {
+                    const int pp = gi.p0 + r;
+                    ar = A.src ? A.src[pp] / A.src_div : pp;
+                    base = A.a; sbase = A.a_scale;
+                }
+                p = base + (size_t)ar * H * EB;
+                if (FP8) ps = sbase + (size_t)ar * (H / 128);
+            } else {
+                const int hr = h_row(A, gi, r);
+                p = A.h + (size_t)hr * I * EB;
+                if (FP8) ps = A.h_scale + (size_t)hr * (I / 128);
+            }
+            rows[tid] = p;
+            srow[tid] = ps;
+            out_row[tid] = (m0 + tid < gi.m) ? (PHASE == 0 ? h_row(A, gi, m0 + tid)
+                                                           : (gi.shared ? m0 + tid : gi.p0 + m0 + tid))
+                                             : -1;
+        } else {
+            const int j = tid - kBigM;                       // 0 .. 255: B rows
+            size_t wrow;
+            const uint8_t* wbase;
+            if (PHASE == 0) {
+                // rows 0..127: gate columns n0..n0+127; 128..255: up columns
+                wrow = (size_t)gi.e * I + n0 + (j & 127);
+                wbase = (const uint8_t*)(j < 128 ? bk.wg : bk.wu);
+            } else {
+                wrow = (size_t)gi.e * H + n0 + j;
+                wbase = (const uint8_t*)bk.wd;
+            }
+            rows[kBigM + j] = wbase + wrow * K * EB;
+        }
+        __syncthreads();
+
+        // rows of this wave that hold data, in 16-row blocks
+        const int nrb = min(max((valid - wm * 128 + 15) / 16, 0), 8);
+
+        f32x4 acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // weight-scale row index of this wave's columns (e4m3)
+        const float* wsc0 = nullptr;
+        const float* wsc1 = nullptr;
+        if (FP8) {
+            if (PHASE == 0) {
+                const size_t b = ((size_t)gi.e * (I / 128) + n0 / 128) * (H / 128);
+                wsc0 = bk.sg + b;   // gate
+                wsc1 = bk.su + b;   // up
+            } else {
+                // this tile spans two 128-column blocks; wave columns wn*64 .. +64
+                wsc0 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128) * (I / 128);
+                wsc1 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128 + 1) * (I / 128);
+            }
+        }
+
+        float sa_next = 0.f;
+        issue_stage(stage_buf, rows, 0, wave, lane);
+        if (FP8 && tid < kBigM) sa_next = srow[tid][0];
+
+        for (int s = 0; s < nstages; ++s) {
+            uint8_t* cur = stage_buf + (s & 1) * kStageBytes;
+            if (FP8) {
+                // scale products of stage s (k-block s) for every row
+                if (tid < kBigM) {
+                    float* sp = sprod + (s & 1) * 2 * kBigM;
+                    sp[tid] = sa_next * wsc0[s];
+                    sp[kBigM + tid] = sa_next * wsc1[s];
+                }
+            }
+            __syncthreads();   // stage s landed for every wave; stage s-1 fully consumed
+            if (s + 1 < nstages) {
+                issue_stage(stage_buf + ((s + 1) & 1) * kStageBytes, rows, (size_t)(s + 1) * kStage, wave, lane);
+                if (FP8 && tid < kBigM) sa_next = srow[tid][s + 1];
+            }
+            const uint8_t* As = cur;
+            const uint8_t* Bs = cur + kBigM * kStage;
+            if (FP8) {
+                const float* sp = sprod + (s & 1) * 2 * kBigM;
+                i32x8 bfr[4];
+                bf16x8 dummy;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // B rows of block j: gate/up: j<2 gate rows wn*32+16j, j>=2 up rows 128+wn*32+16(j-2)
+                    const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2))
+                                                : wn * 64 + 16 * j;
+                    load_frag<DT>(Bs, brow + lane % 16, lane, 0, bfr[j], dummy);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (i < nrb) {
+                        const int rb = wm * 128 + i * 16;
+                        i32x8 afr;
+                        load_frag<DT>(As, rb + lane % 16, lane, 0, afr, dummy);
+                        const f32x4 sc0 = *(const f32x4*)(sp + rb + 4 * (lane / 16));
+                        const f32x4 sc1 = *(const f32x4*)(sp + kBigM + rb + 4 * (lane / 16));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                            const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], z, 0, 0, 0, 127, 0, 127);
+                            // gate/up: blocks 0,1 use gate scales, 2,3 up; down: wave columns are in one 128-block
+                            const bool second = PHASE == 0 ? (j >= 2) : (wn >= 2);
+                            const f32x4 sc = second ? sc1 : sc0;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc[i][j][q]);
+                        }
+                    }
+                    // keep one row block's fragments live at a time (register budget:
+                    // 256 per wave at two waves per SIMD)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8 bfr[4];
+                    i32x8 dummy;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2))
+                                                    : wn * 64 + 16 * j;
+                        load_frag<DT>(Bs, brow + lane % 16, lane, ks, dummy, bfr[j]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (i < nrb) {
+                            bf16x8 afr;
+                            load_frag<DT>(As, wm * 128 + i * 16 + lane % 16, lane, ks, dummy, afr);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---------------------------------------------------------------- epilogue
+        if (PHASE == 0) {
+            // h = silu(gate) * up: blocks j and j+2 hold the same h column
+            float hv[8][2][4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[i][j][q] = silu_mul(acc[i][j][q], acc[i][j + 2][q]);
+            if (FP8) {
+                // amax over the tile's 128 h columns, per row: wave part, then across wn
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float mx = fmaxf(fabsf(hv[i][0][q]), fabsf(hv[i][1][q]));
+#pragma unroll
+                        for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+                        if (lane % 16 == 0) red[wn * kBigM + wm * 128 + i * 16 + 4 * (lane / 16) + q] = mx;
+                    }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
+                    const int hr = out_row[r];
+                    if (hr < 0) continue;
+                    if (FP8) {
+                        const float amax = fmaxf(fmaxf(red[r], red[kBigM + r]), fmaxf(red[2 * kBigM + r], red[3 * kBigM + r]));
+                        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                        if (wn == 0 && lane % 16 == 0) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] / sc);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            ((uint16_t*)A.h)[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] =
+                                (uint16_t)f32_to_bf16_bits(hv[i][j][q]);
+                    }
+                }
+        } else {
+            void* yb = gi.shared ? A.y_sh : A.y;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
+                    const int yr = out_row[r];
+                    if (yr < 0) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + lane % 16;
+                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
+                        else ((float*)yb)[o] = acc[i][j][q];
+                    }
+                }
+        }
+    }
+}
+
+// LDS: 2 stages + 512 row pointers + 256 output rows + 256 scale rows + products + amax partials
+constexpr size_t kBigLds = 2 * kStageBytes + 512 * sizeof(void*) + kBigM * sizeof(int) + kBigM * sizeof(void*) +
+                           2 * 2 * kBigM * sizeof(float) + 4 * kBigM * sizeof(float);
+
+template <int DT, int PHASE>
+static hipError_t launch_big_t(const GArgs& A, const TileList& L, hipStream_t s) {
+    static const int grid = [] {
+        hipFuncSetAttribute((const void*)big_kernel<DT, PHASE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+        return device_cu_count();   // one 512-thread workgroup per CU (LDS-limited)
+    }();
+    hipLaunchKernelGGL((big_kernel<DT, PHASE>), dim3(grid), dim3(512), kBigLds, s, A, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_big_gateup(int dt, const GArgs& A, const TileList& L, hipStream_t s) {
+    return dt == DT_E4M3 ? launch_big_t<DT_E4M3, 0>(A, L, s) : launch_big_t<DT_BF16, 0>(A, L, s);
+}
+
+hipError_t launch_big_down(int dt, const GArgs& A, const TileList& L, hipStream_t s) {
+    return dt == DT_E4M3 ? launch_big_t<DT_E4M3, 1>(A, L, s) : launch_big_t<DT_BF16, 1>(A, L, s);
+}
+
+}  // namespace moe

@@ -107,11 +107,13 @@ struct TileIter {
     __device__ void next() { t += stride; }
 };
 
-// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip).
+// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_stream_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_big_gateup(int dt, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_big_down(int dt, const GArgs& A, const TileList& L, hipStream_t s);
 int device_cu_count();
 
 }  // namespace moe
