@@ -69,6 +69,7 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
                                                          int R_max, ClassSpec cs, ListsOut out) {
     __shared__ int m_of[kMaxGroups];
     __shared__ int cls_of[kMaxGroups];
+    __shared__ int2 mc_of[kMaxGroups];        // (m, class) packed for the rank loop
     __shared__ int rank_of[kMaxGroups];
     __shared__ int nt_by_rank[kClasses][kMaxGroups];
     __shared__ int members[kClasses];
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         c = m > 0 ? c : -1;
         m_of[g] = m;
         cls_of[g] = c;
+        mc_of[g] = make_int2(m, c);
         if (c >= 0) atomicAdd(&members[c], 1);
     }
     __syncthreads();
@@ -99,8 +101,11 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         if (c < 0) continue;
         const int m = m_of[g];
         int rank = 0;
-        for (int o = 0; o < ng; ++o)
-            rank += (cls_of[o] == c && (m_of[o] > m || (m_of[o] == m && o < g)));
+#pragma unroll 16
+        for (int o = 0; o < ng; ++o) {
+            const int2 mc = mc_of[o];
+            rank += (int)((mc.y == c) & ((mc.x > m) | ((mc.x == m) & (o < g))));
+        }
         nt_by_rank[c][rank] = (m + cs.bm[c] - 1) / cs.bm[c];
         rank_of[g] = rank;
     }

@@ -8,7 +8,9 @@
 // the same 128 h columns; down: 256 output columns), K staged 128 bytes at a
 // time in a double-buffered LDS ring fed by direct global->LDS 16-byte loads
 // (no VGPR round trip).  LDS rows are 128 bytes with the eight 16-byte chunks
-// XOR-swizzled by (row & 7) so that MFMA fragment reads spread over the banks.
+// XOR-swizzled by ((row >> 1) & 7): a 16-lane fragment read (16 consecutive
+// rows, one chunk each) then touches each of the 64 banks once (even rows
+// fall in banks 0-31, odd rows in 32-63, eight distinct positions each).
 // 8 waves (2 along M x 4 along N), each computing 128 x 64 with 16x16 MFMA
 // blocks.
 //   e4m3: one v_mfma_scale_f32_16x16x128_f8f6f4 per block and stage covers a
@@ -33,7 +35,7 @@ constexpr int kStageBytes = (kBigM + kBigN) * kStage;   // 64 KiB: A rows then B
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Issue the direct loads of one stage: 512 rows x 8 chunks = 4096 16-byte
 // chunks; every instruction of a wave fills 1 KiB of LDS = 8 rows.
@@ -44,7 +46,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* lds_stage, const uint8_t* c
         const int region = wave * 8 + q;               // 64 regions of 8 rows
         const int row = region * 8 + lane / 8;         // 0 .. 511
         const int pos = lane % 8;                      // chunk position in LDS
-        const int chunk = pos ^ (row & 7);             // chunk of the row stored there
+        const int chunk = pos ^ ((row >> 1) & 7);      // chunk of the row stored there
         const uint8_t* g = rows[row] + k0 + chunk * 16;
         __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds_stage + region * 1024), 16, 0, 0);
     }
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
     float* sprod = (float*)(srow + kBigM);                           // [2 stages][2][256]
     float* red = sprod + 2 * 2 * kBigM;                              // [4][256] amax partials
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // scalar: wave-uniform branches
     const int wm = wave / 4, wn = wave % 4;
 
     for (TileIter it(L, ntn); it.valid(); it.next()) {
@@ -201,14 +204,22 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
                                                 : wn * 64 + 16 * j;
                     load_frag<DT>(Bs, brow + lane % 16, lane, 0, bfr[j], dummy);
                 }
+                // A fragments and row scales run one row block ahead of the MFMAs
+                i32x8 afr;
+                f32x4 sc0, sc1;
+                auto fetch = [&](int i, i32x8& a, f32x4& c0, f32x4& c1) {
+                    const int rb = wm * 128 + i * 16;
+                    load_frag<DT>(As, rb + lane % 16, lane, 0, a, dummy);
+                    c0 = *(const f32x4*)(sp + rb + 4 * (lane / 16));
+                    c1 = *(const f32x4*)(sp + kBigM + rb + 4 * (lane / 16));
+                };
+                if (nrb > 0) fetch(0, afr, sc0, sc1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     if (i < nrb) {
-                        const int rb = wm * 128 + i * 16;
-                        i32x8 afr;
-                        load_frag<DT>(As, rb + lane % 16, lane, 0, afr, dummy);
-                        const f32x4 sc0 = *(const f32x4*)(sp + rb + 4 * (lane / 16));
-                        const f32x4 sc1 = *(const f32x4*)(sp + kBigM + rb + 4 * (lane / 16));
+                        i32x8 afr_n = afr;
+                        f32x4 sc0_n = sc0, sc1_n = sc1;
+                        if (i + 1 < nrb) fetch(i + 1, afr_n, sc0_n, sc1_n);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -219,10 +230,10 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
 #pragma unroll
                             for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc[i][j][q]);
                         }
+                        afr = afr_n;
+                        sc0 = sc0_n;
+                        sc1 = sc1_n;
                     }
-                    // keep one row block's fragments live at a time (register budget:
-                    // 256 per wave at two waves per SIMD)
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
 #pragma unroll

@@ -41,40 +41,68 @@ __global__ __launch_bounds__(kChunk) void perm_hist_kernel(const int32_t* __rest
     for (int e = threadIdx.x; e < E; e += kChunk) chunk_hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads; thread e owns expert e.  Turns chunk_hist
-// into chunk_base in place.
+// One workgroup of 1024 threads turns chunk_hist [nch][E] into chunk_base in
+// place and writes counts / offsets.  TPE threads share an expert (thread
+// e*TPE + j owns the j-th contiguous run of chunks of expert e), so the chunk
+// loops are nch / TPE long and their loads are independent.
+template <int TPE>
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_hist, int nch, int E, int R,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
+    __shared__ int32_t part[1024];     // per-thread partial sums (then their exclusive prefix)
+    __shared__ int32_t tot[1024];      // per-expert totals (then exclusive prefix = offsets)
     __shared__ int32_t wsum[16];
-    const int e = threadIdx.x;
-    int32_t c = 0;
-    if (e < E)
-        for (int ch = 0; ch < nch; ++ch) c += chunk_hist[(size_t)ch * E + e];
-    // exclusive scan of tot over e (1024 entries): wave scans + wave totals
-    const int lane = e % kWave, w = e / kWave;
+    const int tid = threadIdx.x;
+    const int e = tid / TPE, j = tid % TPE;
+    const int run = (nch + TPE - 1) / TPE;
+    const int c0 = min(j * run, nch), c1 = min(c0 + run, nch);
+    int32_t sum = 0;
+    if (e < E) {
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) sum += chunk_hist[(size_t)c * E + e];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    if (j == 0) {
+        int32_t acc = 0;
+        for (int q = 0; q < TPE; ++q) {
+            const int32_t v = part[tid + q];
+            part[tid + q] = acc;
+            acc += v;
+        }
+        tot[e] = e < E ? acc : 0;
+    }
+    __syncthreads();
+    // exclusive scan of tot over experts (1024 entries, one per thread)
+    const int lane = tid % kWave, w = tid / kWave;
+    const int32_t c = tot[tid];
     int32_t v = c;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        int32_t o = __shfl_up(v, d, kWave);
+        const int32_t o = __shfl_up(v, d, kWave);
         if (lane >= d) v += o;
     }
     if (lane == kWave - 1) wsum[w] = v;
     __syncthreads();
-    int32_t wbase = 0;
-    for (int i = 0; i < w; ++i) wbase += wsum[i];
-    const int32_t excl = wbase + v - c;
+    int32_t wb = 0;
+    for (int i = 0; i < w; ++i) wb += wsum[i];
+    __syncthreads();
+    tot[tid] = wb + v - c;            // exclusive prefix over experts
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = wb + v - c;
+    }
+    if (tid == 0) offsets[E] = R;
+    __syncthreads();
     if (e < E) {
-        counts[e] = c;
-        offsets[e] = excl;
-        int32_t run = excl;
-        for (int ch = 0; ch < nch; ++ch) {
-            const int32_t h = chunk_hist[(size_t)ch * E + e];
-            chunk_hist[(size_t)ch * E + e] = run;
-            run += h;
+        int32_t base = tot[e] + part[tid];
+#pragma unroll 8
+        for (int cc = c0; cc < c1; ++cc) {
+            const int32_t h = chunk_hist[(size_t)cc * E + e];
+            chunk_hist[(size_t)cc * E + e] = base;
+            base += h;
         }
     }
-    if (e == 0) offsets[E] = R;
 }
 
 __global__ __launch_bounds__(kChunk) void perm_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
@@ -117,7 +145,17 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int
     if (nch > 0) {
         hipLaunchKernelGGL(perm_hist_kernel, dim3(nch), dim3(kChunk), 0, s, ids, R, E, chunk);
     }
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, chunk, nch, E, R, counts, offsets);
+    // threads per expert: the largest power of two with E * TPE <= 1024
+#define MOE_SCAN(TPEV) hipLaunchKernelGGL(perm_scan_kernel<TPEV>, dim3(1), dim3(1024), 0, s, chunk, nch, E, R, counts, offsets)
+    if (E <= 8) MOE_SCAN(128);
+    else if (E <= 16) MOE_SCAN(64);
+    else if (E <= 32) MOE_SCAN(32);
+    else if (E <= 64) MOE_SCAN(16);
+    else if (E <= 128) MOE_SCAN(8);
+    else if (E <= 256) MOE_SCAN(4);
+    else if (E <= 512) MOE_SCAN(2);
+    else MOE_SCAN(1);
+#undef MOE_SCAN
     if (nch > 0) {
         hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(kChunk), 0, s, ids, R, E, nbits, chunk, src, dest);
     }

@@ -15,18 +15,76 @@
 
 namespace moe {
 
-constexpr int kRouterKC = 32;   // h values staged in LDS per step
-
-template <int RT, int RE, bool XBF16>
+// Tile: TT = 16*RT tokens x TE = 16*RE experts per 256-thread workgroup, each
+// thread owning RT x RE logits.  h is consumed in chunks of KC: while the
+// chunk in LDS is being used, the next one is already loaded into registers,
+// and it is written to the other LDS buffer afterwards (one barrier per
+// chunk).  Loads are 16-byte vectors; rows and columns past T and E are
+// clamped to valid ones (their logits are computed and discarded), so the
+// staging has no branches.  x is stored transposed ([h][token]) with
+// consecutive threads on consecutive tokens (conflict-free).
+template <int RT, int RE, int KC, bool XBF16, bool WVEC>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv, int T, int H,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ bias, int E,
                                                             float* __restrict__ logits) {
-    constexpr int TT = 16 * RT, TE = 16 * RE, KC = kRouterKC;
-    __shared__ float xs[KC][TT];
-    __shared__ float wsm[KC][TE];
+    constexpr int TT = 16 * RT, TE = 16 * RE;
+    constexpr int NXV = TT * KC / 8 / 256;          // 8-element x vectors per thread
+    constexpr int NWV = KC * TE / 4 / 256;          // 4-element W vectors per thread
+    static_assert(NXV * 2048 == TT * KC && NWV * 1024 == KC * TE, "tile");
+    __shared__ float xs[2][KC][TT];
+    __shared__ __attribute__((aligned(16))) float wsm[2][KC][TE];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int t0 = blockIdx.y * TT, e0 = blockIdx.x * TE;
+
+    float rx[NXV][8];
+    f32x4 rw[NWV];
+    auto fetch = [&](int h0) {
+#pragma unroll
+        for (int v = 0; v < NXV; ++v) {
+            const int idx = tid + v * 256, r = idx % TT, cg = idx / TT;
+            const size_t off = (size_t)min(t0 + r, T - 1) * H + h0 + cg * 8;
+            if (XBF16) {
+                const uint4 u = *(const uint4*)((const uint16_t*)xv + off);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    rx[v][2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+                    rx[v][2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+                }
+            } else {
+                const float4 a = *(const float4*)((const float*)xv + off);
+                const float4 b = *(const float4*)((const float*)xv + off + 4);
+                rx[v][0] = a.x; rx[v][1] = a.y; rx[v][2] = a.z; rx[v][3] = a.w;
+                rx[v][4] = b.x; rx[v][5] = b.y; rx[v][6] = b.z; rx[v][7] = b.w;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) {
+            const int idx = tid + v * 256, c = idx / (TE / 4), q4 = idx % (TE / 4);
+            const float* row = wr + (size_t)(h0 + c) * E;
+            if (WVEC) {
+                rw[v] = *(const f32x4*)(row + min(e0 + q4 * 4, E - 4));
+            } else {
+                const int e = e0 + q4 * 4;
+                rw[v] = f32x4{row[min(e, E - 1)], row[min(e + 1, E - 1)], row[min(e + 2, E - 1)],
+                              row[min(e + 3, E - 1)]};
+            }
+        }
+    };
+    auto stash = [&](int b) {
+#pragma unroll
+        for (int v = 0; v < NXV; ++v) {
+            const int idx = tid + v * 256, r = idx % TT, cg = idx / TT;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xs[b][cg * 8 + q][r] = rx[v][q];
+        }
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) {
+            const int idx = tid + v * 256, c = idx / (TE / 4), q4 = idx % (TE / 4);
+            *(f32x4*)&wsm[b][c][q4 * 4] = rw[v];
+        }
+    };
 
     float acc[RT][RE];
 #pragma unroll
@@ -34,35 +92,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 #pragma unroll
         for (int j = 0; j < RE; ++j) acc[i][j] = 0.0f;
 
-    for (int h0 = 0; h0 < H; h0 += KC) {
-        // stage x[t0 .. t0+TT)[h0 .. h0+KC) transposed, coalesced along h
-        for (int i = tid; i < TT * KC; i += 256) {
-            const int r = i / KC, c = i % KC, t = t0 + r;
-            float v = 0.0f;
-            if (t < T) {
-                const size_t off = (size_t)t * H + h0 + c;
-                v = XBF16 ? bf16_bits_to_f32(((const uint16_t*)xv)[off]) : ((const float*)xv)[off];
-            }
-            xs[c][r] = v;
-        }
-        // stage Wr[h0 .. h0+KC)[e0 .. e0+TE), coalesced along e
-        for (int i = tid; i < KC * TE; i += 256) {
-            const int c = i / TE, q = i % TE, e = e0 + q;
-            wsm[c][q] = (e < E) ? wr[(size_t)(h0 + c) * E + e] : 0.0f;
-        }
-        __syncthreads();
+    const int nch = H / KC;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int b = ch & 1;
+        if (ch + 1 < nch) fetch((ch + 1) * KC);
 #pragma unroll 8
         for (int c = 0; c < KC; ++c) {
-            float a[RT], b[RE];
+            float a[RT], w[RE];
 #pragma unroll
-            for (int i = 0; i < RT; ++i) a[i] = xs[c][ty * RT + i];
+            for (int i = 0; i < RT; ++i) a[i] = xs[b][c][ty * RT + i];
 #pragma unroll
-            for (int j = 0; j < RE; ++j) b[j] = wsm[c][tx * RE + j];
+            for (int j = 0; j < RE; ++j) w[j] = wsm[b][c][tx * RE + j];
 #pragma unroll
             for (int i = 0; i < RT; ++i)
 #pragma unroll
-                for (int j = 0; j < RE; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < RE; ++j) acc[i][j] = __builtin_fmaf(a[i], w[j], acc[i][j]);
         }
+        if (ch + 1 < nch) stash(b ^ 1);
         __syncthreads();
     }
 #pragma unroll
@@ -80,25 +129,28 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
 }
 
-template <int RT, int RE>
+template <int RT, int RE, int KC>
 static hipError_t launch_rl(const void* x, int xb, int T, int H, const float* wr, const float* bias,
                             int E, float* logits, hipStream_t s) {
     dim3 grid((E + 16 * RE - 1) / (16 * RE), (T + 16 * RT - 1) / (16 * RT));
-    if (xb)
-        hipLaunchKernelGGL((router_logits_kernel<RT, RE, true>), grid, dim3(256), 0, s, x, T, H, wr, bias, E, logits);
-    else
-        hipLaunchKernelGGL((router_logits_kernel<RT, RE, false>), grid, dim3(256), 0, s, x, T, H, wr, bias, E, logits);
+    const bool wvec = E % 4 == 0 && ((uintptr_t)wr & 15) == 0;
+#define MOE_RL(XB, WV) hipLaunchKernelGGL((router_logits_kernel<RT, RE, KC, XB, WV>), grid, dim3(256), 0, s, x, T, H, wr, bias, E, logits)
+    if (xb) { if (wvec) MOE_RL(true, true); else MOE_RL(true, false); }
+    else { if (wvec) MOE_RL(false, true); else MOE_RL(false, false); }
+#undef MOE_RL
     return hipGetLastError();
 }
 
 hipError_t launch_router_logits(const void* x, int x_bf16, int T, int H, const float* wr,
                                 const float* bias, int E, float* logits, hipStream_t s) {
-    // Larger register tiles raise FMA:LDS ratio; small T keeps one logit per
-    // thread so that enough chains run in parallel.
+    // Large batches: big register tiles (FMA:LDS ratio).  Small batches: one
+    // logit per thread so that enough chains run side by side, and long h
+    // chunks so that each chunk's work covers the memory latency.  H is a
+    // multiple of 128, so every KC below divides it.
     const long chains = (long)T * E;
-    if (chains >= (1L << 21) && E >= 64) return launch_rl<8, 4>(x, x_bf16, T, H, wr, bias, E, logits, s);
-    if (chains >= (1L << 18)) return launch_rl<4, 2>(x, x_bf16, T, H, wr, bias, E, logits, s);
-    return launch_rl<1, 1>(x, x_bf16, T, H, wr, bias, E, logits, s);
+    if (chains >= (1L << 21) && E >= 64) return launch_rl<8, 4, 32>(x, x_bf16, T, H, wr, bias, E, logits, s);
+    if (chains >= (1L << 18)) return launch_rl<4, 2, 64>(x, x_bf16, T, H, wr, bias, E, logits, s);
+    return launch_rl<1, 1, 128>(x, x_bf16, T, H, wr, bias, E, logits, s);
 }
 
 // ---- top-k + weights: one wave per token ----------------------------------
@@ -106,8 +158,9 @@ hipError_t launch_router_logits(const void* x, int x_bf16, int T, int H, const f
 // 64-bit key (order-preserving logit bits << 32 | (0xFFFFFFFF - e)), so the
 // wave maximum is the largest logit and, among equal logits, the lowest e.
 constexpr int kTopkWaves = 4;
-constexpr int kMaxSlots = 16;   // E <= 1024
 
+// NS = logits per lane (E <= 64 * NS)
+template <int NS>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                           int k, int sigmoid, int32_t* __restrict__ ids,
                                                           float* __restrict__ wout) {
@@ -116,9 +169,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     const int t = blockIdx.x * kTopkWaves + wave;
     const bool valid = t < T;          // no early return: the barrier below needs every wave
     const float* lt = logits + (size_t)(valid ? t : 0) * E;
-    uint64_t key[kMaxSlots];
+    uint64_t key[NS];
 #pragma unroll
-    for (int s = 0; s < kMaxSlots; ++s) {
+    for (int s = 0; s < NS; ++s) {
         const int e = s * kWave + lane;
         key[s] = 0;
         if (valid && e < E) key[s] = ((uint64_t)f32_order_key(lt[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
@@ -126,12 +179,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     for (int j = 0; j < (valid ? k : 0); ++j) {
         uint64_t best = 0;
 #pragma unroll
-        for (int s = 0; s < kMaxSlots; ++s) best = key[s] > best ? key[s] : best;
+        for (int s = 0; s < NS; ++s) best = key[s] > best ? key[s] : best;
         best = wave_max_u64(best);
         const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
         if ((e & (kWave - 1)) == lane) {
 #pragma unroll
-            for (int s = 0; s < kMaxSlots; ++s)
+            for (int s = 0; s < NS; ++s)
                 if (s == (e >> 6)) key[s] = 0;
         }
         if (lane == 0) sel[wave][j] = e;
@@ -159,7 +212,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int sigmoid, int32_t* ids,
                               float* w, hipStream_t s) {
     dim3 grid((T + kTopkWaves - 1) / kTopkWaves);
-    hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, s, logits, T, E, k, sigmoid, ids, w);
+#define MOE_TOPK(NSV) hipLaunchKernelGGL(router_topk_kernel<NSV>, grid, dim3(256), 0, s, logits, T, E, k, sigmoid, ids, w)
+    if (E <= 64) MOE_TOPK(1);
+    else if (E <= 128) MOE_TOPK(2);
+    else if (E <= 256) MOE_TOPK(4);
+    else if (E <= 512) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
     return hipGetLastError();
 }
 
