@@ -261,11 +261,12 @@ def moe_layer(wl, want_intermediates: bool = False) -> dict:
     return res
 
 
-def moe_layer_tokens(wl, tokens, expert_cache=None) -> dict:
+def moe_layer_tokens(wl, tokens) -> dict:
     """Outputs for a subset of tokens only.  A token's routing and output
     depend on that token alone (the permutation only reorders work), so each
     sampled output is computed directly: out[t] = y_sh(x_t) +
-    sum_j w[t][j] y_{ids[t][j]}(x_t)."""
+    sum_j w[t][j] y_{ids[t][j]}(x_t).  Experts are visited one at a time
+    (only one expert's weights are held on the host at once)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x32, wr, b = layer_inputs(wl)
     xs = x32[tokens]
@@ -273,18 +274,13 @@ def moe_layer_tokens(wl, tokens, expert_cache=None) -> dict:
     a = activation_rows(wl, xs)
     hm = h_mode_for(wl.w_dt)
     y_dt = "bf16" if wl.out_dt == "bf16" else "f32"
-    cache = {} if expert_cache is None else expert_cache
     out = np.zeros((len(tokens), wl.H))
     if wl.shared is not None:
-        if "shared" not in cache:
-            cache["shared"] = bank_expert_f64(wl.shared, 0)
-        out += round_to(expert_ffn(a, *cache["shared"], hm), y_dt)
+        out += round_to(expert_ffn(a, *bank_expert_f64(wl.shared, 0), hm), y_dt)
     ys = {}
     for e in sorted(set(int(e) for e in ids.reshape(-1))):
-        if e not in cache:
-            cache[e] = bank_expert_f64(wl.routed, e)
         rows_t, rows_j = np.nonzero(ids == e)
-        ye = round_to(expert_ffn(a[rows_t], *cache[e], hm), y_dt)
+        ye = round_to(expert_ffn(a[rows_t], *bank_expert_f64(wl.routed, e), hm), y_dt)
         for r, (t, j) in enumerate(zip(rows_t, rows_j)):
             ys[(t, j)] = ye[r]
     for t in range(len(tokens)):          # combine in slot order j = 0 .. k-1

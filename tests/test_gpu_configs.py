@@ -1,0 +1,117 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times (the layer as its C-ABI calls, bench.LayerRunner /
+GroupedRunner).
+
+Routing (expert ids) and the permutation (counts, offsets, src, dest) are
+compared bit-exactly over every token against the oracle; routing weights
+within 1e-6.  Layer outputs are compared on sampled tokens (or, for the
+pre-routed workload, sampled rows of every group) that the oracle computes one
+by one: max-abs <= 2e-2 and rel-Frobenius <= 1e-2 for fp32/bf16 weights,
+rel-Frobenius <= 3e-2 for fp8 weights.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+from oracle import moe as om  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _check(got, ref, fp8, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rf = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    ma = float(np.abs(got - ref).max())
+    print(f"[{what}] rel_frob={rf:.3e} max_abs={ma:.3e} max|ref|={np.abs(ref).max():.3e}", flush=True)
+    assert np.isfinite(got).all()
+    if fp8:
+        assert rf <= 3e-2
+    else:
+        assert rf <= 1e-2 and ma <= 2e-2
+
+
+def _sample(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, T - 1] + rng.choice(T, size=n, replace=False).tolist()))
+
+
+@pytest.mark.parametrize("cid,nsample", [(1, None), (2, 6), (3, 6), (5, 4)])
+def test_layer_config_full_size(cid, nsample):
+    print(f"config {cid}: generating", flush=True)
+    wl = synth.config(cid, device=DEV)
+    run = bench.LayerRunner(wl, DEV)
+    for _, f in run.calls():
+        f()
+    torch.cuda.synchronize()
+    ids = run.ids.cpu().numpy()
+    print(f"config {cid}: oracle routing over {wl.T} tokens", flush=True)
+    x32, wr, b = om.layer_inputs(wl)
+    ids_ref, w_ref, _ = om.route(x32, wr, b, wl.k, wl.score)
+    np.testing.assert_array_equal(ids, ids_ref)
+    assert np.abs(run.w.cpu().numpy() - w_ref).max() <= 1e-6
+    counts, offsets, src, dest = om.permute(ids_ref, wl.E)
+    np.testing.assert_array_equal(run.counts.cpu().numpy(), counts)
+    np.testing.assert_array_equal(run.offsets.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(run.src.cpu().numpy(), src)
+    np.testing.assert_array_equal(run.dest.cpu().numpy(), dest)
+    out = run.out.float().cpu().numpy()
+    fp8 = wl.w_dt == "e4m3"
+    if nsample is None:
+        ref = om.moe_layer(wl)
+        _check(out, ref["out"], fp8, f"config {cid} all tokens")
+    else:
+        toks = _sample(wl.T, nsample, cid)
+        print(f"config {cid}: oracle outputs for tokens {toks}", flush=True)
+        ref = om.moe_layer_tokens(wl, toks)
+        np.testing.assert_array_equal(ref["ids"], ids_ref[toks])
+        _check(out[toks], ref["out"], fp8, f"config {cid} tokens {toks}")
+
+
+def test_grouped_config_full_size():
+    print("config 4: generating", flush=True)
+    wl = synth.config(4, device=DEV)
+    run = bench.GroupedRunner(wl, DEV)
+    for _, f in run.calls():
+        f()
+    torch.cuda.synchronize()
+    y = run.y.float().cpu().numpy()
+    y_sh = run.y_sh.float().cpu().numpy()
+    rng = np.random.default_rng(4)
+    sample = {}
+    for g, m in enumerate(wl.group_m):
+        sample[g] = sorted(set([0, m - 1] + rng.choice(m, 2, replace=False).tolist()))
+    sample["shared"] = sorted(set([0, wl.shared_m - 1] + rng.choice(wl.shared_m, 2, replace=False).tolist()))
+    print("config 4: oracle rows", flush=True)
+    ref = om.grouped_ffn(wl, group_sample=sample)
+    starts = np.concatenate([[0], np.cumsum(wl.group_m)])
+    got, want = [], []
+    for g in range(len(wl.group_m)):
+        rows, yr = ref[g]
+        got.append(y[starts[g] + rows])
+        want.append(yr)
+    rows, yr = ref["shared"]
+    got.append(y_sh[rows])
+    want.append(yr)
+    _check(np.concatenate(got), np.concatenate(want), True, "config 4 sampled rows")
+
+
+def test_layer_full_size_is_deterministic():
+    wl = synth.config(2, device=DEV)
+    run = bench.LayerRunner(wl, DEV)
+    outs = []
+    for _ in range(2):
+        for _, f in run.calls():
+            f()
+        torch.cuda.synchronize()
+        outs.append(run.out.clone())
+    assert torch.equal(outs[0], outs[1])
