@@ -11,15 +11,20 @@
 // XOR-swizzled by ((row >> 1) & 7): a 16-lane fragment read (16 consecutive
 // rows, one chunk each) then touches each of the 64 banks once (even rows
 // fall in banks 0-31, odd rows in 32-63, eight distinct positions each).
-// 8 waves (2 along M x 4 along N), each computing 128 x 64 with 16x16 MFMA
-// blocks.
-//   e4m3: one v_mfma_scale_f32_16x16x128_f8f6f4 per block and stage covers a
-//         whole 128-wide scaling block; its partial is added to the fp32
-//         accumulator with one FMA by (activation scale x weight scale), the
-//         products being formed once per row and stage in LDS.
-//   bf16: two v_mfma_f32_16x16x32_bf16 per block and stage, no scaling.
+// 8 waves (2 along M x 4 along N), each computing 128 x 64.
+//   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 (unit MX scales), one per 16x16
+//         block and stage: a whole 128-wide scaling block.  Its partial joins
+//         the fp32 accumulator with one FMA by (activation scale x weight
+//         scale); the products are formed once per row and stage in LDS.
+//   bf16: v_mfma_f32_32x32x16_bf16 (the 16x16x32 form runs at half rate on
+//         gfx950), four per 32x32 block and stage.
 // The gate/up epilogue applies SwiGLU and quantises h per row and 128-column
 // block (e4m3) or rounds it (bf16); the down epilogue writes y.
+//
+// Full tiles (256 rows) run a branch-free body with the A fragments
+// double-buffered by name; the last, partial m-tile of a group runs a body
+// that skips empty 16-row blocks.  They are separate instantiations so each
+// gets its own register allocation.
 //
 // Tiles of a group are ordered n-tile-major with the group's m-tiles
 // innermost, so the m-tiles that share a weight tile run side by side on one
@@ -34,12 +39,12 @@ constexpr int kStage = 128;       // K bytes per stage
 constexpr int kStageBytes = (kBigM + kBigN) * kStage;   // 64 KiB: A rows then B rows
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Issue the direct loads of one stage: 512 rows x 8 chunks = 4096 16-byte
 // chunks; every instruction of a wave fills 1 KiB of LDS = 8 rows.
-// arow[r] / brow[r]: row base pointers (already offset to k0 = 0).
 __device__ __forceinline__ void issue_stage(uint8_t* lds_stage, const uint8_t* const* rows, size_t k0, int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -52,15 +57,248 @@ __device__ __forceinline__ void issue_stage(uint8_t* lds_stage, const uint8_t* c
     }
 }
 
-template <int DT>
-__device__ __forceinline__ void load_frag(const uint8_t* base, int row, int lane, int step, i32x8& f8, bf16x8& f16) {
-    if (DT == DT_E4M3) {
-        const int c0 = 2 * (lane / 16);
-        const i32x4 lo = *(const i32x4*)(base + swz(row, c0));
-        const i32x4 hi = *(const i32x4*)(base + swz(row, c0 + 1));
-        f8 = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+// 32-byte e4m3 fragment (16x16x128 operand): row, bytes [32*(lane/16), +32)
+__device__ __forceinline__ i32x8 frag8(const uint8_t* base, int row, int lane) {
+    const int c0 = 2 * (lane / 16);
+    const i32x4 lo = *(const i32x4*)(base + swz(row, c0));
+    const i32x4 hi = *(const i32x4*)(base + swz(row, c0 + 1));
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// 16-byte bf16 fragment (32x32x16 operand, k-step ks of 4): row, bytes [32*ks + 16*(lane/32), +16)
+__device__ __forceinline__ bf16x8 frag16(const uint8_t* base, int row, int lane, int ks) {
+    return *(const bf16x8*)(base + swz(row, ks * 2 + lane / 32));
+}
+
+struct BigSmem {
+    uint8_t* stage_buf;           // 2 x 64 KiB
+    const uint8_t** rows;         // 512 row pointers (A rows, then B rows)
+    int* out_row;                 // 256 output rows (-1: none)
+    const float** srow;           // 256 activation-scale rows (e4m3)
+    float* sprod;                 // [2 stages][2][256] scale products
+    float* red;                   // [4][256] amax partials
+};
+
+// One tile: K loop and epilogue.  FULL: all 256 rows hold data.
+template <int DT, int PHASE, bool FULL>
+__device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, const Bank& bk, const BigSmem& S,
+                                         int n0, int valid, int tid, int lane, int wave, int wm, int wn) {
+    constexpr bool FP8 = DT == DT_E4M3;
+    constexpr int EB = FP8 ? 1 : 2;
+    const int H = A.H, I = A.I;
+    const int K = PHASE == 0 ? H : I;
+    const int nstages = K * EB / kStage;
+    // 16-row blocks of this wave that hold data
+    const int nrb = FULL ? 8 : min(max((valid - wm * 128 + 15) / 16, 0), 8);
+
+    // weight-scale rows of this tile (e4m3): gate/up: gate and up of column
+    // block n0/128; down: the two 128-column blocks of the tile
+    const float* wsc0 = nullptr;
+    const float* wsc1 = nullptr;
+    if (FP8) {
+        if (PHASE == 0) {
+            const size_t b = ((size_t)gi.e * (I / 128) + n0 / 128) * (H / 128);
+            wsc0 = bk.sg + b;
+            wsc1 = bk.su + b;
+        } else {
+            wsc0 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128) * (I / 128);
+            wsc1 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128 + 1) * (I / 128);
+        }
+    }
+
+    // accumulators: e4m3 16x16 blocks [8][4]; bf16 32x32 blocks [4][2]
+    f32x4 acc8[FP8 ? 8 : 1][4];
+    f32x16 acc16[FP8 ? 1 : 4][2];
+    if (FP8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc8[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-        f16 = *(const bf16x8*)(base + swz(row, step * 4 + lane / 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc16[i][j] = f32x16{};
+    }
+
+    float sa_next = 0.f;
+    issue_stage(S.stage_buf, S.rows, 0, wave, lane);
+    if (FP8 && tid < kBigM) sa_next = S.srow[tid][0];
+
+    for (int s = 0; s < nstages; ++s) {
+        const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
+        if (FP8 && tid < kBigM) {
+            float* sp = S.sprod + (s & 1) * 2 * kBigM;
+            sp[tid] = sa_next * wsc0[s];
+            sp[kBigM + tid] = sa_next * wsc1[s];
+        }
+        __syncthreads();   // stage s landed for every wave; stage s-1 fully consumed
+        if (s + 1 < nstages) {
+            issue_stage(S.stage_buf + ((s + 1) & 1) * kStageBytes, S.rows, (size_t)(s + 1) * kStage, wave, lane);
+            if (FP8 && tid < kBigM) sa_next = S.srow[tid][s + 1];
+        }
+        const uint8_t* As = cur;
+        const uint8_t* Bs = cur + kBigM * kStage;
+        if (FP8) {
+            const float* sp = S.sprod + (s & 1) * 2 * kBigM;
+            // B rows of block j: gate/up: j<2 gate rows wn*32+16j, j>=2 up rows 128+wn*32+16(j-2)
+            i32x8 bfr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2)) : wn * 64 + 16 * j;
+                bfr[j] = frag8(Bs, brow + lane % 16, lane);
+            }
+            // scale products: gate/up blocks 0,1 use the gate products, 2,3 the up
+            // products; in the down phase a wave's four blocks lie in one
+            // 128-column block (wn < 2: the first)
+            const float* sp0 = sp + (PHASE == 0 ? 0 : (wn >= 2 ? kBigM : 0));
+            const float* sp1 = sp + kBigM;
+            auto fetch = [&](int i, i32x8& a, f32x4& c0, f32x4& c1) {
+                const int rb = wm * 128 + i * 16;
+                a = frag8(As, rb + lane % 16, lane);
+                c0 = *(const f32x4*)(sp0 + rb + 4 * (lane / 16));
+                if (PHASE == 0) c1 = *(const f32x4*)(sp1 + rb + 4 * (lane / 16));
+            };
+            auto block = [&](int i, const i32x8& a, const f32x4& c0, const f32x4& c1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bfr[j], z, 0, 0, 0, 127, 0, 127);
+                    const f32x4& sc = (PHASE == 0 && j >= 2) ? c1 : c0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc8[i][j][q]);
+                }
+            };
+            if (FULL) {
+                i32x8 a0, a1;
+                f32x4 c00, c01, c10, c11;
+                fetch(0, a0, c00, c01);
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    fetch(i + 1, a1, c10, c11);
+                    block(i, a0, c00, c01);
+                    if (i + 2 < 8) fetch(i + 2, a0, c00, c01);
+                    block(i + 1, a1, c10, c11);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (i < nrb) {
+                        i32x8 a;
+                        f32x4 c0, c1;
+                        fetch(i, a, c0, c1);
+                        block(i, a, c0, c1);
+                    }
+                }
+            }
+        } else {
+            // bf16: 32x32 blocks; B block j: gate/up j=0 gate rows wn*32.., j=1 up rows 128+wn*32..;
+            // down: rows wn*64 + 32j
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 bfr[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int brow = PHASE == 0 ? (j == 0 ? wn * 32 : 128 + wn * 32) : wn * 64 + 32 * j;
+                    bfr[j] = frag16(Bs, brow + lane % 32, lane, ks);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (FULL || 2 * i < nrb) {
+                        const bf16x8 a = frag16(As, wm * 128 + i * 32 + lane % 32, lane, ks);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[j], acc16[i][j], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // element (i, j, v) of the wave's 128 x 64 accumulator:
+    //   e4m3 16x16: row 16 i + 4 (lane/16) + v, col 16 j + lane%16   (v < 4)
+    //   bf16 32x32: row 32 i + 8 (v/4) + 4 (lane/32) + v%4, col 32 j + lane%32   (v < 16)
+    if (PHASE == 0) {
+        // h = silu(gate) * up for the wave's 32 h columns
+        if (FP8) {
+            float hv[8][2][4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[i][j][q] = silu_mul(acc8[i][j][q], acc8[i][j + 2][q]);
+            // amax over the tile's 128 h columns per row: the wave's part, then across wn
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float mx = fmaxf(fabsf(hv[i][0][q]), fabsf(hv[i][1][q]));
+#pragma unroll
+                    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+                    if (lane % 16 == 0) S.red[wn * kBigM + wm * 128 + i * 16 + 4 * (lane / 16) + q] = mx;
+                }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
+                    const int hr = S.out_row[r];
+                    if (hr < 0) continue;
+                    const float amax = fmaxf(fmaxf(S.red[r], S.red[kBigM + r]), fmaxf(S.red[2 * kBigM + r], S.red[3 * kBigM + r]));
+                    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                    if (wn == 0 && lane % 16 == 0) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] / sc);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * 128 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
+                    const int hr = S.out_row[r];
+                    if (hr < 0) continue;
+                    ((uint16_t*)A.h)[(size_t)hr * I + n0 + wn * 32 + lane % 32] =
+                        (uint16_t)f32_to_bf16_bits(silu_mul(acc16[i][0][v], acc16[i][1][v]));
+                }
+        }
+    } else {
+        void* yb = gi.shared ? A.y_sh : A.y;
+        if (FP8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
+                    const int yr = S.out_row[r];
+                    if (yr < 0) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + lane % 16;
+                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc8[i][j][q]);
+                        else ((float*)yb)[o] = acc8[i][j][q];
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * 128 + i * 32 + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
+                    const int yr = S.out_row[r];
+                    if (yr < 0) continue;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const size_t o = (size_t)yr * H + n0 + wn * 64 + 32 * j + lane % 32;
+                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc16[i][j][v]);
+                        else ((float*)yb)[o] = acc16[i][j][v];
+                    }
+                }
+        }
     }
 }
 
@@ -74,16 +312,15 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
     const int NOUT = PHASE == 0 ? I : H;               // output columns of the phase
     const int ncol = PHASE == 0 ? kBigN / 2 : kBigN;   // output columns per tile
     const int ntn = NOUT / ncol;
-    const int nstages = K * EB / kStage;
-    const int nkb = K / 128;
 
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    uint8_t* stage_buf = smem;                                       // 2 x 64 KiB
-    const uint8_t** rows = (const uint8_t**)(smem + 2 * kStageBytes); // 512 row pointers
-    int* out_row = (int*)(rows + 512);                               // 256 output rows (-1: none)
-    const float** srow = (const float**)(out_row + kBigM);           // 256 activation-scale rows
-    float* sprod = (float*)(srow + kBigM);                           // [2 stages][2][256]
-    float* red = sprod + 2 * 2 * kBigM;                              // [4][256] amax partials
+    BigSmem S;
+    S.stage_buf = smem;
+    S.rows = (const uint8_t**)(smem + 2 * kStageBytes);
+    S.out_row = (int*)(S.rows + 512);
+    S.srow = (const float**)(S.out_row + kBigM);
+    S.sprod = (float*)(S.srow + kBigM);
+    S.red = S.sprod + 2 * 2 * kBigM;
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // scalar: wave-uniform branches
@@ -127,11 +364,11 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
                 p = A.h + (size_t)hr * I * EB;
                 if (FP8) ps = A.h_scale + (size_t)hr * (I / 128);
             }
-            rows[tid] = p;
-            srow[tid] = ps;
-            out_row[tid] = (m0 + tid < gi.m) ? (PHASE == 0 ? h_row(A, gi, m0 + tid)
-                                                           : (gi.shared ? m0 + tid : gi.p0 + m0 + tid))
-                                             : -1;
+            S.rows[tid] = p;
+            S.srow[tid] = ps;
+            S.out_row[tid] = (m0 + tid < gi.m) ? (PHASE == 0 ? h_row(A, gi, m0 + tid)
+                                                             : (gi.shared ? m0 + tid : gi.p0 + m0 + tid))
+                                               : -1;
         } else {
             const int j = tid - kBigM;                       // 0 .. 255: B rows
             size_t wrow;
@@ -144,183 +381,12 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
                 wrow = (size_t)gi.e * H + n0 + j;
                 wbase = (const uint8_t*)bk.wd;
             }
-            rows[kBigM + j] = wbase + wrow * K * EB;
+            S.rows[kBigM + j] = wbase + wrow * K * EB;
         }
         __syncthreads();
 
-        // rows of this wave that hold data, in 16-row blocks
-        const int nrb = min(max((valid - wm * 128 + 15) / 16, 0), 8);
-
-        f32x4 acc[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // weight-scale row index of this wave's columns (e4m3)
-        const float* wsc0 = nullptr;
-        const float* wsc1 = nullptr;
-        if (FP8) {
-            if (PHASE == 0) {
-                const size_t b = ((size_t)gi.e * (I / 128) + n0 / 128) * (H / 128);
-                wsc0 = bk.sg + b;   // gate
-                wsc1 = bk.su + b;   // up
-            } else {
-                // this tile spans two 128-column blocks; wave columns wn*64 .. +64
-                wsc0 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128) * (I / 128);
-                wsc1 = bk.sd + ((size_t)gi.e * (H / 128) + n0 / 128 + 1) * (I / 128);
-            }
-        }
-
-        float sa_next = 0.f;
-        issue_stage(stage_buf, rows, 0, wave, lane);
-        if (FP8 && tid < kBigM) sa_next = srow[tid][0];
-
-        for (int s = 0; s < nstages; ++s) {
-            uint8_t* cur = stage_buf + (s & 1) * kStageBytes;
-            if (FP8) {
-                // scale products of stage s (k-block s) for every row
-                if (tid < kBigM) {
-                    float* sp = sprod + (s & 1) * 2 * kBigM;
-                    sp[tid] = sa_next * wsc0[s];
-                    sp[kBigM + tid] = sa_next * wsc1[s];
-                }
-            }
-            __syncthreads();   // stage s landed for every wave; stage s-1 fully consumed
-            if (s + 1 < nstages) {
-                issue_stage(stage_buf + ((s + 1) & 1) * kStageBytes, rows, (size_t)(s + 1) * kStage, wave, lane);
-                if (FP8 && tid < kBigM) sa_next = srow[tid][s + 1];
-            }
-            const uint8_t* As = cur;
-            const uint8_t* Bs = cur + kBigM * kStage;
-            if (FP8) {
-                const float* sp = sprod + (s & 1) * 2 * kBigM;
-                i32x8 bfr[4];
-                bf16x8 dummy;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // B rows of block j: gate/up: j<2 gate rows wn*32+16j, j>=2 up rows 128+wn*32+16(j-2)
-                    const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2))
-                                                : wn * 64 + 16 * j;
-                    load_frag<DT>(Bs, brow + lane % 16, lane, 0, bfr[j], dummy);
-                }
-                // A fragments and row scales run one row block ahead of the MFMAs
-                i32x8 afr;
-                f32x4 sc0, sc1;
-                auto fetch = [&](int i, i32x8& a, f32x4& c0, f32x4& c1) {
-                    const int rb = wm * 128 + i * 16;
-                    load_frag<DT>(As, rb + lane % 16, lane, 0, a, dummy);
-                    c0 = *(const f32x4*)(sp + rb + 4 * (lane / 16));
-                    c1 = *(const f32x4*)(sp + kBigM + rb + 4 * (lane / 16));
-                };
-                if (nrb > 0) fetch(0, afr, sc0, sc1);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (i < nrb) {
-                        i32x8 afr_n = afr;
-                        f32x4 sc0_n = sc0, sc1_n = sc1;
-                        if (i + 1 < nrb) fetch(i + 1, afr_n, sc0_n, sc1_n);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                            const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], z, 0, 0, 0, 127, 0, 127);
-                            // gate/up: blocks 0,1 use gate scales, 2,3 up; down: wave columns are in one 128-block
-                            const bool second = PHASE == 0 ? (j >= 2) : (wn >= 2);
-                            const f32x4 sc = second ? sc1 : sc0;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc[i][j][q]);
-                        }
-                        afr = afr_n;
-                        sc0 = sc0_n;
-                        sc1 = sc1_n;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 bfr[4];
-                    i32x8 dummy;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2))
-                                                    : wn * 64 + 16 * j;
-                        load_frag<DT>(Bs, brow + lane % 16, lane, ks, dummy, bfr[j]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        if (i < nrb) {
-                            bf16x8 afr;
-                            load_frag<DT>(As, wm * 128 + i * 16 + lane % 16, lane, ks, dummy, afr);
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-        }
-
-        // ---------------------------------------------------------------- epilogue
-        if (PHASE == 0) {
-            // h = silu(gate) * up: blocks j and j+2 hold the same h column
-            float hv[8][2][4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[i][j][q] = silu_mul(acc[i][j][q], acc[i][j + 2][q]);
-            if (FP8) {
-                // amax over the tile's 128 h columns, per row: wave part, then across wn
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float mx = fmaxf(fabsf(hv[i][0][q]), fabsf(hv[i][1][q]));
-#pragma unroll
-                        for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-                        if (lane % 16 == 0) red[wn * kBigM + wm * 128 + i * 16 + 4 * (lane / 16) + q] = mx;
-                    }
-                __syncthreads();
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
-                    const int hr = out_row[r];
-                    if (hr < 0) continue;
-                    if (FP8) {
-                        const float amax = fmaxf(fmaxf(red[r], red[kBigM + r]), fmaxf(red[2 * kBigM + r], red[3 * kBigM + r]));
-                        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-                        if (wn == 0 && lane % 16 == 0) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] / sc);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            ((uint16_t*)A.h)[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] =
-                                (uint16_t)f32_to_bf16_bits(hv[i][j][q]);
-                    }
-                }
-        } else {
-            void* yb = gi.shared ? A.y_sh : A.y;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
-                    const int yr = out_row[r];
-                    if (yr < 0) continue;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + lane % 16;
-                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
-                        else ((float*)yb)[o] = acc[i][j][q];
-                    }
-                }
-        }
+        if (valid == kBigM) big_tile<DT, PHASE, true>(A, gi, bk, S, n0, valid, tid, lane, wave, wm, wn);
+        else big_tile<DT, PHASE, false>(A, gi, bk, S, n0, valid, tid, lane, wave, wm, wn);
     }
 }
 
