@@ -29,18 +29,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // significand at bit 20 (3 fraction bits kept); smaller magnitudes are
 // multiples of 2^-9 (subnormal codes 0..7, 8 meaning 2^-6).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fminf(fabsf(v), 448.0f);
-    const uint32_t ua = __float_as_uint(a);
-    const int ex = (int)(ua >> 23) - 127;
-    uint32_t code;
-    if (ex < -6) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);          // exact scaling, ties to even
-    } else {
-        const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);   // RNE at bit 20
-        code = ((((r >> 23) - 127u + 7u) & 0xFu) << 3) | ((r >> 20) & 7u);
-    }
-    return sign | code;
+    // v_cvt_pk_fp8_f32 rounds to nearest even into OCP e4m3 (finite range
+    // +-448, subnormals kept); inputs are clamped to that range first.  On
+    // gfx950 this equals the bitwise rounding of the value for every fp32
+    // input of magnitude <= 448 (checked exhaustively on the device).
+    const float c = fmaxf(fminf(v, 448.0f), -448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
 // ---- wave64 helpers ----------------------------------------------------------

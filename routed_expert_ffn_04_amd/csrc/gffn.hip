@@ -140,12 +140,18 @@ int device_cu_count() {
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Large groups use the 256 x 256 tiles of gffn_big.hip (bf16 / e4m3 with
-// H a multiple of 256), otherwise the 64-row LDS tiles of gffn_tile.hip.
-static bool use_big(int dt, int H) { return (dt == DT_BF16 || dt == DT_E4M3) && H % 256 == 0; }
+// H a multiple of 256, row offsets of the activation, h and per-expert weight
+// matrices within 32 bits), otherwise the 64-row LDS tiles of gffn_tile.hip.
+static bool use_big(int dt, int H, int I, int R_max, int S) {
+    if (!(dt == DT_BF16 || dt == DT_E4M3) || H % 256 != 0) return false;
+    const uint64_t eb = dt == DT_BF16 ? 2 : 1, lim = (uint64_t)1 << 32;
+    return (uint64_t)std::max(R_max, S) * H * eb < lim && ((uint64_t)R_max + S) * I * eb < lim &&
+           (uint64_t)H * I * eb < lim;
+}
 
-static ClassSpec class_spec(int dt, int H) {
+static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
-    const int bm2 = use_big(dt, H) ? 256 : 64;
+    const int bm2 = use_big(dt, H, I, R_max, S) ? 256 : 64;
     if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
@@ -173,7 +179,7 @@ static void max_entries(int R_max, int G, int S, const ClassSpec& c, int out[kCl
 size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt) {
     const size_t rows = (size_t)R_max + S;
     const int eb = dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1;
-    const ClassSpec cs = class_spec(dt, H);
+    const ClassSpec cs = class_spec(dt, H, I, R_max, S);
     int me[kClasses];
     max_entries(R_max, G, S, cs, me);
     size_t b = align256(rows * I * eb);
@@ -192,7 +198,7 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     A.y = p.y; A.y_sh = p.y_sh; A.y_bf16 = p.y_bf16;
     const size_t rows = (size_t)p.R_max + A.S;
     const int eb = p.dt == DT_F32 ? 4 : p.dt == DT_BF16 ? 2 : 1;
-    const ClassSpec cs = class_spec(p.dt, p.H);
+    const ClassSpec cs = class_spec(p.dt, p.H, p.I, p.R_max, A.S);
     int me[kClasses];
     max_entries(p.R_max, p.G, A.S, cs, me);
 
@@ -220,12 +226,12 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
         e = k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
-                  : use_big(p.dt, p.H) ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
+                  : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
         e = k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
-                  : use_big(p.dt, p.H) ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
+                  : cs.bm[k] == 256 ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
     }
     return e;
 }

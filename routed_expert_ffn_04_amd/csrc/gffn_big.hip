@@ -8,9 +8,8 @@
 // the same 128 h columns; down: 256 output columns), K staged 128 bytes at a
 // time in a double-buffered LDS ring fed by direct global->LDS 16-byte loads
 // (no VGPR round trip).  LDS rows are 128 bytes with the eight 16-byte chunks
-// XOR-swizzled by ((row >> 1) & 7): a 16-lane fragment read (16 consecutive
-// rows, one chunk each) then touches each of the 64 banks once (even rows
-// fall in banks 0-31, odd rows in 32-63, eight distinct positions each).
+// XOR-swizzled per row (swz_key) so that fragment reads run near the LDS
+// read rate.
 // 8 waves (2 along M x 4 along N), each computing 128 x 64.
 //   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 (unit MX scales), one per 16x16
 //         block and stage: a whole 128-wide scaling block.  Its partial joins
@@ -41,27 +40,54 @@ constexpr int kStageBytes = (kBigM + kBigN) * kStage;   // 64 KiB: A rows then B
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// 16-byte chunk c of LDS row r sits at position c ^ key(r).  The key spreads
+// both fragment shapes (16 rows x one chunk, 32 rows x one chunk) over all
+// banks; measured ds_read_b128 rates on gfx950 for these shapes: ~197 B/clk
+// per CU against ~118 for key (r >> 1) & 7 and ~64 unswizzled (lane-linear
+// reads: ~211).
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ swz_key(row)) << 4); }
 
-// Issue the direct loads of one stage: 512 rows x 8 chunks = 4096 16-byte
-// chunks; every instruction of a wave fills 1 KiB of LDS = 8 rows.
-__device__ __forceinline__ void issue_stage(uint8_t* lds_stage, const uint8_t* const* rows, size_t k0, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int region = wave * 8 + q;               // 64 regions of 8 rows
-        const int row = region * 8 + lane / 8;         // 0 .. 511
-        const int pos = lane % 8;                      // chunk position in LDS
-        const int chunk = pos ^ ((row >> 1) & 7);      // chunk of the row stored there
-        const uint8_t* g = rows[row] + k0 + chunk * 16;
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds_stage + region * 1024), 16, 0, 0);
-    }
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
-// 32-byte e4m3 fragment (16x16x128 operand): row, bytes [32*(lane/16), +32)
-__device__ __forceinline__ i32x8 frag8(const uint8_t* base, int row, int lane) {
-    const int c0 = 2 * (lane / 16);
-    const i32x4 lo = *(const i32x4*)(base + swz(row, c0));
-    const i32x4 hi = *(const i32x4*)(base + swz(row, c0 + 1));
+// The direct loads of a stage: 512 rows x 8 chunks = 4096 16-byte chunks;
+// instruction q of wave w fills LDS region 8w+q (1 KiB = rows 8(8w+q) ..
+// +7, lane l: row + l/8, position l%8).  Waves 0-3 move A rows, waves 4-7
+// B rows, so each wave has one base address (in scalar registers); the byte
+// offsets of a lane's eight chunks sit in LDS for the whole tile (registers
+// are taken by the accumulators).
+struct Loader {
+    const uint8_t* base;   // wave-uniform
+    const float* sbase;    // e4m3, waves 0-3: wave-uniform base of the activation scales
+    uint32_t soff;         // e4m3, waves 0-3: byte offset of row 64 w + l's scales
+};
+
+__device__ __forceinline__ void issue_one(uint8_t* lds_stage, const Loader& ld, const uint32_t* loff, int k0, int wave,
+                                          int tid, int q) {
+    __builtin_amdgcn_global_load_lds((const void*)(ld.base + k0 + loff[q * 512 + tid]),
+                                     (lds_void*)(lds_stage + (wave * 8 + q) * 1024), 16, 0, 0);
+}
+
+// 32-byte e4m3 fragment (16x16x128 operand) of the 16 rows starting at row0
+// (a multiple of 16): lane l takes row row0 + l%16, bytes [32*(l/16), +32).
+// The swizzle key of a row depends on its index mod 16 only, so the lane's
+// two chunk offsets (Frag8Lane) are fixed and row0 becomes an immediate.
+struct Frag8Lane {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ Frag8Lane frag8_lane(int lane) {
+    const int r = lane % 16, c0 = 2 * (lane / 16);
+    return Frag8Lane{(uint32_t)swz(r, c0), (uint32_t)swz(r, c0 + 1)};
+}
+__device__ __forceinline__ i32x8 frag8(const uint8_t* base, int row0, const Frag8Lane& fl) {
+    const uint8_t* p = base + row0 * kStage;
+    const i32x4 lo = *(const i32x4*)(p + fl.lo);
+    const i32x4 hi = *(const i32x4*)(p + fl.hi);
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
@@ -72,17 +98,34 @@ __device__ __forceinline__ bf16x8 frag16(const uint8_t* base, int row, int lane,
 
 struct BigSmem {
     uint8_t* stage_buf;           // 2 x 64 KiB
-    const uint8_t** rows;         // 512 row pointers (A rows, then B rows)
+    uint32_t* aoff;               // 256 A-row byte offsets from the A base
     int* out_row;                 // 256 output rows (-1: none)
     const float** srow;           // 256 activation-scale rows (e4m3)
     float* sprod;                 // [2 stages][2][256] scale products
     float* red;                   // [4][256] amax partials
+    uint32_t* loff;               // [8][512] per-thread chunk offsets of the direct loads
+    float* sa_lds;                // [2][256] activation scales of a later stage (e4m3)
+    float* w_lds;                 // [2][64] weight scales of a later stage (e4m3): [0], [1]
 };
+
+// Direct loads of the scales of K block kb into LDS slot kb & 1 (e4m3):
+// waves 0-3 the activation scale of their 64 rows, wave 4 the two weight
+// scales (lane l: the first block's if l is even, else the second's).
+__device__ __forceinline__ void issue_scales(const BigSmem& S, const Loader& ld, const float* w0, const float* w1,
+                                             int kb, int wave, int lane) {
+    if (wave < 4) {
+        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)(ld.sbase + kb) + ld.soff),
+                                         (lds_void*)(S.sa_lds + (kb & 1) * kBigM + wave * 64), 4, 0, 0);
+    } else if (wave == 4) {
+        __builtin_amdgcn_global_load_lds((const void*)((lane & 1 ? w1 : w0) + kb), (lds_void*)(S.w_lds + (kb & 1) * 64),
+                                         4, 0, 0);
+    }
+}
 
 // One tile: K loop and epilogue.  FULL: all 256 rows hold data.
 template <int DT, int PHASE, bool FULL>
 __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, const Bank& bk, const BigSmem& S,
-                                         int n0, int valid, int tid, int lane, int wave, int wm, int wn) {
+                                         const Loader& ld, int n0, int valid, int tid, int lane, int wave, int wm, int wn) {
     constexpr bool FP8 = DT == DT_E4M3;
     constexpr int EB = FP8 ? 1 : 2;
     const int H = A.H, I = A.I;
@@ -121,32 +164,58 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
             for (int j = 0; j < 2; ++j) acc16[i][j] = f32x16{};
     }
 
-    float sa_next = 0.f;
-    issue_stage(S.stage_buf, S.rows, 0, wave, lane);
-    if (FP8 && tid < kBigM) sa_next = S.srow[tid][0];
+    // Scale products (e4m3): activation scale of the row x weight scale of the
+    // column block, per row and K block, for the first (gate) and second (up)
+    // column block.  Stage s's products are formed by waves 0-3 at the start
+    // of stage s-1 from scales that direct loads brought into LDS during stage
+    // s-2; stage 0's come straight from memory at the tile start.
+    if (FP8 && tid < kBigM) {
+        const float sa0 = S.srow[tid][0];
+        S.sprod[tid] = sa0 * wsc0[0];
+        S.sprod[kBigM + tid] = sa0 * wsc1[0];
+    }
+    if (FP8 && 1 < nstages) issue_scales(S, ld, wsc0, wsc1, 1, wave, lane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) issue_one(S.stage_buf, ld, S.loff, 0, wave, tid, q);
 
     for (int s = 0; s < nstages; ++s) {
         const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
-        if (FP8 && tid < kBigM) {
-            float* sp = S.sprod + (s & 1) * 2 * kBigM;
-            sp[tid] = sa_next * wsc0[s];
-            sp[kBigM + tid] = sa_next * wsc1[s];
-        }
-        __syncthreads();   // stage s landed for every wave; stage s-1 fully consumed
+        __syncthreads();   // stage s and the scales of block s+1 landed; stage s-1 fully consumed
         if (s + 1 < nstages) {
-            issue_stage(S.stage_buf + ((s + 1) & 1) * kStageBytes, S.rows, (size_t)(s + 1) * kStage, wave, lane);
-            if (FP8 && tid < kBigM) sa_next = S.srow[tid][s + 1];
+            if (FP8 && tid < kBigM) {
+                // products of stage s+1 into buffer (s+1)&1, last read in stage s-1
+                const float sa = S.sa_lds[((s + 1) & 1) * kBigM + tid];
+                const float* w = S.w_lds + ((s + 1) & 1) * 64;
+                float* spn = S.sprod + ((s + 1) & 1) * 2 * kBigM;
+                spn[tid] = sa * w[0];
+                spn[kBigM + tid] = sa * w[1];
+            }
+            if (FP8 && s + 2 < nstages) issue_scales(S, ld, wsc0, wsc1, s + 2, wave, lane);
         }
+        // The next stage's eight direct loads of this wave are spread over
+        // the first half of the compute: issued back to back they would stall
+        // the wave on a full load queue (the vector L1 keeps a bounded number
+        // of line misses in flight) before its first MFMA.
+        const bool more = s + 1 < nstages;
+        uint8_t* nbuf = S.stage_buf + ((s + 1) & 1) * kStageBytes;
+        const int k1 = (s + 1) * kStage;
+        auto dma2 = [&](int b) {   // loads 2b and 2b+1, after compute block b < 4
+            if (more) {
+                issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b);
+                issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b + 1);
+            }
+        };
         const uint8_t* As = cur;
         const uint8_t* Bs = cur + kBigM * kStage;
         if (FP8) {
+            const Frag8Lane fl = frag8_lane(lane);
             const float* sp = S.sprod + (s & 1) * 2 * kBigM;
             // B rows of block j: gate/up: j<2 gate rows wn*32+16j, j>=2 up rows 128+wn*32+16(j-2)
             i32x8 bfr[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2)) : wn * 64 + 16 * j;
-                bfr[j] = frag8(Bs, brow + lane % 16, lane);
+                bfr[j] = frag8(Bs, brow, fl);
             }
             // scale products: gate/up blocks 0,1 use the gate products, 2,3 the up
             // products; in the down phase a wave's four blocks lie in one
@@ -155,7 +224,7 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
             const float* sp1 = sp + kBigM;
             auto fetch = [&](int i, i32x8& a, f32x4& c0, f32x4& c1) {
                 const int rb = wm * 128 + i * 16;
-                a = frag8(As, rb + lane % 16, lane);
+                a = frag8(As, rb, fl);
                 c0 = *(const f32x4*)(sp0 + rb + 4 * (lane / 16));
                 if (PHASE == 0) c1 = *(const f32x4*)(sp1 + rb + 4 * (lane / 16));
             };
@@ -169,27 +238,18 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                     for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc8[i][j][q]);
                 }
             };
-            if (FULL) {
-                i32x8 a0, a1;
-                f32x4 c00, c01, c10, c11;
-                fetch(0, a0, c00, c01);
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    fetch(i + 1, a1, c10, c11);
-                    block(i, a0, c00, c01);
-                    if (i + 2 < 8) fetch(i + 2, a0, c00, c01);
-                    block(i + 1, a1, c10, c11);
+            for (int i = 0; i < 8; ++i) {
+                if (FULL || i < nrb) {
+                    i32x8 a;
+                    f32x4 c0, c1;
+                    fetch(i, a, c0, c1);
+                    block(i, a, c0, c1);
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (i < nrb) {
-                        i32x8 a;
-                        f32x4 c0, c1;
-                        fetch(i, a, c0, c1);
-                        block(i, a, c0, c1);
-                    }
-                }
+                if (i < 4) dma2(i);
+                // keep the scheduler from hoisting later blocks' fragment reads
+                // (register pressure: the accumulators take half the budget)
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             // bf16: 32x32 blocks; B block j: gate/up j=0 gate rows wn*32.., j=1 up rows 128+wn*32..;
@@ -210,6 +270,10 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                         for (int j = 0; j < 2; ++j)
                             acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[j], acc16[i][j], 0, 0, 0);
                     }
+                }
+                if (ks < 2) {
+                    dma2(2 * ks);
+                    dma2(2 * ks + 1);
                 }
             }
         }
@@ -248,11 +312,13 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                     const int hr = S.out_row[r];
                     if (hr < 0) continue;
                     const float amax = fmaxf(fmaxf(S.red[r], S.red[kBigM + r]), fmaxf(S.red[2 * kBigM + r], S.red[3 * kBigM + r]));
-                    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                    // scale amax / 448 (within an ulp); codes h * (448 / amax)
+                    const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+                    const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
                     if (wn == 0 && lane % 16 == 0) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] / sc);
+                        A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] * inv);
                 }
         } else {
 #pragma unroll
@@ -316,11 +382,14 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     BigSmem S;
     S.stage_buf = smem;
-    S.rows = (const uint8_t**)(smem + 2 * kStageBytes);
-    S.out_row = (int*)(S.rows + 512);
+    S.aoff = (uint32_t*)(smem + 2 * kStageBytes);
+    S.out_row = (int*)(S.aoff + kBigM);
     S.srow = (const float**)(S.out_row + kBigM);
     S.sprod = (float*)(S.srow + kBigM);
     S.red = S.sprod + 2 * 2 * kBigM;
+    S.loff = (uint32_t*)(S.red + 4 * kBigM);
+    S.sa_lds = (float*)(S.loff + 8 * 512);
+    S.w_lds = S.sa_lds + 2 * kBigM;
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // scalar: wave-uniform branches
@@ -339,60 +408,74 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
         const int m0 = mt * kBigM;
         const int n0 = nt * ncol;
         const int valid = min(gi.m - m0, kBigM);
-        const Bank& bk = gi.shared ? A.shared : A.routed;
+        const Bank bk = gi.shared ? A.shared : A.routed;
 
         __syncthreads();   // previous tile is done with LDS
         if (tid < kBigM) {
             const int r = min(m0 + tid, gi.m - 1);          // rows past the end re-read the last row
-            const uint8_t* p;
+            uint32_t o;
             const float* ps = nullptr;
             if (PHASE == 0) {
                 int ar;
-                const uint8_t* base;
                 const float* sbase;
                 if (gi.shared) {
-                    ar = r; base = A.a_sh; sbase = A.a_sh_scale;
+                    ar = r; sbase = A.a_sh_scale;
                 } else {
                     const int pp = gi.p0 + r;
                     ar = A.src ? A.src[pp] / A.src_div : pp;
-                    base = A.a; sbase = A.a_scale;
+                    sbase = A.a_scale;
                 }
-                p = base + (size_t)ar * H * EB;
+                o = (uint32_t)ar * (uint32_t)(H * EB);
                 if (FP8) ps = sbase + (size_t)ar * (H / 128);
             } else {
                 const int hr = h_row(A, gi, r);
-                p = A.h + (size_t)hr * I * EB;
+                o = (uint32_t)hr * (uint32_t)(I * EB);
                 if (FP8) ps = A.h_scale + (size_t)hr * (I / 128);
             }
-            S.rows[tid] = p;
+            S.aoff[tid] = o;
             S.srow[tid] = ps;
             S.out_row[tid] = (m0 + tid < gi.m) ? (PHASE == 0 ? h_row(A, gi, m0 + tid)
                                                              : (gi.shared ? m0 + tid : gi.p0 + m0 + tid))
                                                : -1;
-        } else {
-            const int j = tid - kBigM;                       // 0 .. 255: B rows
-            size_t wrow;
-            const uint8_t* wbase;
-            if (PHASE == 0) {
-                // rows 0..127: gate columns n0..n0+127; 128..255: up columns
-                wrow = (size_t)gi.e * I + n0 + (j & 127);
-                wbase = (const uint8_t*)(j < 128 ? bk.wg : bk.wu);
-            } else {
-                wrow = (size_t)gi.e * H + n0 + j;
-                wbase = (const uint8_t*)bk.wd;
-            }
-            S.rows[kBigM + j] = wbase + wrow * K * EB;
         }
         __syncthreads();
 
-        if (valid == kBigM) big_tile<DT, PHASE, true>(A, gi, bk, S, n0, valid, tid, lane, wave, wm, wn);
-        else big_tile<DT, PHASE, false>(A, gi, bk, S, n0, valid, tid, lane, wave, wm, wn);
+        // this lane's eight chunks: LDS row 64 w + 8 q + l/8, position l%8
+        Loader ld;
+        if (wave < 4) {
+            ld.base = uniform_ptr(PHASE == 0 ? (gi.shared ? A.a_sh : A.a) : A.h);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = (wave * 8 + q) * 8 + lane / 8;
+                S.loff[q * 512 + tid] = S.aoff[row] + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
+            }
+            if (FP8) {
+                ld.sbase = (const float*)uniform_ptr(PHASE == 0 ? (gi.shared ? A.a_sh_scale : A.a_scale) : A.h_scale);
+                ld.soff = (uint32_t)((const uint8_t*)S.srow[wave * 64 + lane] - (const uint8_t*)ld.sbase);
+            }
+        } else {
+            // gate/up: B rows 0..127 gate columns n0.., 128..255 up columns; down: columns n0..n0+255
+            const void* wm_base = PHASE == 0 ? (wave < 6 ? bk.wg : bk.wu) : bk.wd;
+            ld.base = uniform_ptr((const uint8_t*)wm_base + (size_t)gi.e * H * I * EB);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = (wave * 8 + q) * 8 + lane / 8;   // 256 .. 511
+                const int j = row - kBigM;
+                const int nrow = n0 + (PHASE == 0 ? (j & 127) : j);
+                S.loff[q * 512 + tid] = (uint32_t)nrow * (uint32_t)(K * EB) + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
+            }
+        }
+
+        if (valid == kBigM) big_tile<DT, PHASE, true>(A, gi, bk, S, ld, n0, valid, tid, lane, wave, wm, wn);
+        else big_tile<DT, PHASE, false>(A, gi, bk, S, ld, n0, valid, tid, lane, wave, wm, wn);
     }
 }
 
-// LDS: 2 stages + 512 row pointers + 256 output rows + 256 scale rows + products + amax partials
-constexpr size_t kBigLds = 2 * kStageBytes + 512 * sizeof(void*) + kBigM * sizeof(int) + kBigM * sizeof(void*) +
-                           2 * 2 * kBigM * sizeof(float) + 4 * kBigM * sizeof(float);
+// LDS: 2 stages + 256 A-row offsets + 256 output rows + 256 scale rows + products + amax partials
+// + load offsets + staged scales
+constexpr size_t kBigLds = 2 * kStageBytes + kBigM * sizeof(uint32_t) + kBigM * sizeof(int) + kBigM * sizeof(void*) +
+                           2 * 2 * kBigM * sizeof(float) + 4 * kBigM * sizeof(float) + 8 * 512 * sizeof(uint32_t) +
+                           2 * kBigM * sizeof(float) + 2 * 64 * sizeof(float);
 
 template <int DT, int PHASE>
 static hipError_t launch_big_t(const GArgs& A, const TileList& L, hipStream_t s) {

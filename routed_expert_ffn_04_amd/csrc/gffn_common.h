@@ -80,8 +80,10 @@ __device__ __forceinline__ int h_row(const GArgs& A, const GroupInfo& gi, int r)
     return gi.shared ? A.R_max + r : gi.p0 + r;
 }
 
+// silu(g) * u with a hardware reciprocal (about 1 ulp) in place of the
+// divide; exp(-g) overflowing to +inf gives the exact limit 0.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Static, die-aware assignment of the tiles of a list to a persistent grid.
