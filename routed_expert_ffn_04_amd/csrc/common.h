@@ -37,6 +37,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
+// four values to four e4m3 codes, little-endian in one word
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+    a = fmaxf(fminf(a, 448.0f), -448.0f);
+    b = fmaxf(fminf(b, 448.0f), -448.0f);
+    c = fmaxf(fminf(c, 448.0f), -448.0f);
+    d = fmaxf(fminf(d, 448.0f), -448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // ---- wave64 helpers ----------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

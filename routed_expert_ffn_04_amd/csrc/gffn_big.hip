@@ -96,6 +96,13 @@ __device__ __forceinline__ bf16x8 frag16(const uint8_t* base, int row, int lane,
     return *(const bf16x8*)(base + swz(row, ks * 2 + lane / 32));
 }
 
+// position of token t = 128 wm + 16 i + c's scale product within a
+// 256-entry kind block: [wm][i / 4][c][i % 4], so that the 16 lanes reading
+// one quarter read 256 contiguous bytes
+__device__ __forceinline__ int prod_index(int t) {
+    return (t & ~127) + ((t & 127) >> 6) * 64 + (t & 15) * 4 + (((t & 127) >> 4) & 3);
+}
+
 struct BigSmem {
     uint8_t* stage_buf;           // 2 x 64 KiB
     uint32_t* aoff;               // 256 A-row byte offsets from the A base
@@ -169,10 +176,12 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
     // column block.  Stage s's products are formed by waves 0-3 at the start
     // of stage s-1 from scales that direct loads brought into LDS during stage
     // s-2; stage 0's come straight from memory at the tile start.
+    // Products are stored per token at [kind][prod_index(t)], so a lane reads
+    // the eight of its token column with two 16-byte loads.
     if (FP8 && tid < kBigM) {
         const float sa0 = S.srow[tid][0];
-        S.sprod[tid] = sa0 * wsc0[0];
-        S.sprod[kBigM + tid] = sa0 * wsc1[0];
+        S.sprod[prod_index(tid)] = sa0 * wsc0[0];
+        S.sprod[kBigM + prod_index(tid)] = sa0 * wsc1[0];
     }
     if (FP8 && 1 < nstages) issue_scales(S, ld, wsc0, wsc1, 1, wave, lane);
 #pragma unroll
@@ -187,8 +196,8 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                 const float sa = S.sa_lds[((s + 1) & 1) * kBigM + tid];
                 const float* w = S.w_lds + ((s + 1) & 1) * 64;
                 float* spn = S.sprod + ((s + 1) & 1) * 2 * kBigM;
-                spn[tid] = sa * w[0];
-                spn[kBigM + tid] = sa * w[1];
+                spn[prod_index(tid)] = sa * w[0];
+                spn[kBigM + prod_index(tid)] = sa * w[1];
             }
             if (FP8 && s + 2 < nstages) issue_scales(S, ld, wsc0, wsc1, s + 2, wave, lane);
         }
@@ -208,43 +217,43 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
         const uint8_t* As = cur;
         const uint8_t* Bs = cur + kBigM * kStage;
         if (FP8) {
+            // D^T = W X^T: the MFMA row operand is a 16-column weight block,
+            // the column operand a 16-token block; a lane accumulates columns
+            // 4 (l/16) + q of the weight block for token l%16.
             const Frag8Lane fl = frag8_lane(lane);
-            const float* sp = S.sprod + (s & 1) * 2 * kBigM;
-            // B rows of block j: gate/up: j<2 gate rows wn*32+16j, j>=2 up rows 128+wn*32+16(j-2)
-            i32x8 bfr[4];
+            // weight blocks j: gate/up j<2 gate columns wn*32+16j, j>=2 up columns; down wn*64+16j
+            i32x8 wfr[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2)) : wn * 64 + 16 * j;
-                bfr[j] = frag8(Bs, brow, fl);
+                wfr[j] = frag8(Bs, brow, fl);
             }
-            // scale products: gate/up blocks 0,1 use the gate products, 2,3 the up
-            // products; in the down phase a wave's four blocks lie in one
-            // 128-column block (wn < 2: the first)
-            const float* sp0 = sp + (PHASE == 0 ? 0 : (wn >= 2 ? kBigM : 0));
-            const float* sp1 = sp + kBigM;
-            auto fetch = [&](int i, i32x8& a, f32x4& c0, f32x4& c1) {
-                const int rb = wm * 128 + i * 16;
-                a = frag8(As, rb, fl);
-                c0 = *(const f32x4*)(sp0 + rb + 4 * (lane / 16));
-                if (PHASE == 0) c1 = *(const f32x4*)(sp1 + rb + 4 * (lane / 16));
-            };
-            auto block = [&](int i, const i32x8& a, const f32x4& c0, const f32x4& c1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bfr[j], z, 0, 0, 0, 127, 0, 127);
-                    const f32x4& sc = (PHASE == 0 && j >= 2) ? c1 : c0;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], sc[q], acc8[i][j][q]);
-                }
-            };
+            // scale products of this lane's token in the eight token blocks:
+            // gate/up: kind 0 (gate) for j<2, kind 1 (up) for j>=2; down: the
+            // kind of the wave's 128-column block (wn >= 2: the second)
+            const float* sp = S.sprod + (s & 1) * 2 * kBigM + wm * 128 + (lane % 16) * 4;
+            const int k0i = PHASE == 0 ? 0 : (wn >= 2 ? 1 : 0);
+            const f32x4 g0 = *(const f32x4*)(sp + k0i * kBigM);
+            const f32x4 g1 = *(const f32x4*)(sp + k0i * kBigM + 64);
+            f32x4 u0 = g0, u1 = g1;
+            if (PHASE == 0) {
+                u0 = *(const f32x4*)(sp + kBigM);
+                u1 = *(const f32x4*)(sp + kBigM + 64);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if (FULL || i < nrb) {
-                    i32x8 a;
-                    f32x4 c0, c1;
-                    fetch(i, a, c0, c1);
-                    block(i, a, c0, c1);
+                    const i32x8 x = frag8(As, wm * 128 + i * 16, fl);
+                    const float cg = i < 4 ? g0[i & 3] : g1[i & 3];
+                    const float cu = i < 4 ? u0[i & 3] : u1[i & 3];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], x, z, 0, 0, 0, 127, 0, 127);
+                        const float c = (PHASE == 0 && j >= 2) ? cu : cg;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], c, acc8[i][j][q]);
+                    }
                 }
                 if (i < 4) dma2(i);
                 // keep the scheduler from hoisting later blocks' fragment reads
@@ -281,7 +290,7 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
 
     // ---------------------------------------------------------------- epilogue
     // element (i, j, v) of the wave's 128 x 64 accumulator:
-    //   e4m3 16x16: row 16 i + 4 (lane/16) + v, col 16 j + lane%16   (v < 4)
+    //   e4m3 16x16 (transposed): row 16 i + lane%16, col 16 j + 4 (lane/16) + v   (v < 4)
     //   bf16 32x32: row 32 i + 8 (v/4) + 4 (lane/32) + v%4, col 32 j + lane%32   (v < 16)
     if (PHASE == 0) {
         // h = silu(gate) * up for the wave's 32 h columns
@@ -293,33 +302,35 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) hv[i][j][q] = silu_mul(acc8[i][j][q], acc8[i][j + 2][q]);
-            // amax over the tile's 128 h columns per row: the wave's part, then across wn
+            // amax over the tile's 128 h columns per row: the lane's eight,
+            // the four lanes of the row (l/16), then the four wn waves
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                float mx = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float mx = fmaxf(fabsf(hv[i][0][q]), fabsf(hv[i][1][q]));
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-                    if (lane % 16 == 0) S.red[wn * kBigM + wm * 128 + i * 16 + 4 * (lane / 16) + q] = mx;
-                }
+                    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(hv[i][j][q]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                if (lane < 16) S.red[wn * kBigM + wm * 128 + i * 16 + lane] = mx;
+            }
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                const int r = wm * 128 + i * 16 + lane % 16;
+                const int hr = S.out_row[r];
+                if (hr < 0) continue;
+                const float amax = fmaxf(fmaxf(S.red[r], S.red[kBigM + r]), fmaxf(S.red[2 * kBigM + r], S.red[3 * kBigM + r]));
+                // scale amax / 448 (within an ulp); codes h * (448 / amax)
+                const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+                const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
+                if (wn == 0 && lane < 16) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
-                    const int hr = S.out_row[r];
-                    if (hr < 0) continue;
-                    const float amax = fmaxf(fmaxf(S.red[r], S.red[kBigM + r]), fmaxf(S.red[2 * kBigM + r], S.red[3 * kBigM + r]));
-                    // scale amax / 448 (within an ulp); codes h * (448 / amax)
-                    const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-                    const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
-                    if (wn == 0 && lane % 16 == 0) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        A.h[(size_t)hr * I + n0 + wn * 32 + 16 * j + lane % 16] = (uint8_t)f32_to_e4m3(hv[i][j][q] * inv);
-                }
+                for (int j = 0; j < 2; ++j)
+                    *(uint32_t*)(A.h + (size_t)hr * I + n0 + wn * 32 + 16 * j + 4 * (lane / 16)) =
+                        f32x4_to_e4m3x4(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -336,19 +347,23 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
         void* yb = gi.shared ? A.y_sh : A.y;
         if (FP8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                const int r = wm * 128 + i * 16 + lane % 16;
+                const int yr = S.out_row[r];
+                if (yr < 0) continue;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm * 128 + i * 16 + 4 * (lane / 16) + q;
-                    const int yr = S.out_row[r];
-                    if (yr < 0) continue;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + lane % 16;
-                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc8[i][j][q]);
-                        else ((float*)yb)[o] = acc8[i][j][q];
+                for (int j = 0; j < 4; ++j) {
+                    const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + 4 * (lane / 16);
+                    const f32x4 v = acc8[i][j];
+                    if (A.y_bf16) {
+                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *(uint2*)((uint16_t*)yb + o) = make_uint2(lo, hi);
+                    } else {
+                        *(f32x4*)((float*)yb + o) = v;
                     }
                 }
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
