@@ -23,6 +23,12 @@ namespace moe {
 
 struct ClassSpec {
     int mlo[kClasses], mhi[kClasses], bm[kClasses];
+    // Class 1 (weight-streaming tiles of 64 rows re-read the group's rows once
+    // per 32 output columns) moves into class 2 (256-row tiles) when it has at
+    // least this many members: then there are enough groups to fill the chip
+    // with the large tiles, which read every row once per 128/256 columns.
+    // 0: never.
+    int promote_min;
 };
 
 struct ListsOut {
@@ -96,6 +102,19 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         if (c >= 0) atomicAdd(&members[c], 1);
     }
     __syncthreads();
+    if (cs.promote_min > 0 && members[1] >= cs.promote_min) {
+        for (int g = tid; g < ng; g += 1024)
+            if (cls_of[g] == 1) {
+                cls_of[g] = 2;
+                mc_of[g].y = 2;
+            }
+        __syncthreads();
+        if (tid == 0) {
+            members[2] += members[1];
+            members[1] = 0;
+        }
+        __syncthreads();
+    }
     for (int g = tid; g < ng; g += 1024) {
         const int c = cls_of[g];
         if (c < 0) continue;
@@ -149,6 +168,8 @@ static bool use_big(int dt, int H, int I, int R_max, int S) {
            (uint64_t)H * I * eb < lim;
 }
 
+constexpr int kPromoteMin = 32;
+
 static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
     const int bm2 = use_big(dt, H, I, R_max, S) ? 256 : 64;
@@ -156,6 +177,7 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
+        c.promote_min = bm2 == 256 ? kPromoteMin : 0;
     } else {
         c.mlo[0] = 0;  c.mhi[0] = 0;        c.bm[0] = 16;   // unused
         c.mlo[1] = 0;  c.mhi[1] = 0;        c.bm[1] = 64;   // unused
@@ -171,7 +193,9 @@ static void max_entries(int R_max, int G, int S, const ClassSpec& c, int out[kCl
     for (int k = 0; k < kClasses; ++k) {
         if (c.mhi[k] <= c.mlo[k]) { out[k] = 0; continue; }
         // each member group has m > mlo, so at most rows / (mlo+1) of them
-        const long members = std::min(groups, rows / (c.mlo[k] + 1));
+        // (class 2 may also receive class 1's groups)
+        const int lo = (k == 2 && c.promote_min > 0) ? c.mlo[1] : c.mlo[k];
+        const long members = std::min(groups, rows / (lo + 1));
         out[k] = (int)std::min<long>(rows / c.bm[k] + members, 1L << 30);
     }
 }

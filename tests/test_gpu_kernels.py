@@ -151,6 +151,10 @@ GROUPED_CASES = [
     ([130, 5, 0, 64, 1], 40, 256, 256, "e4m3"),
     ([257, 9], 300, 512, 384, "e4m3"),
     ([70, 0, 12], 20, 256, 256, "f32"),
+    # 36 groups of 17..116 rows: enough 17..256-row groups to move them from
+    # the weight-streaming tiles to the 256-row tiles (and 31: just too few)
+    ([17 + (g * 37) % 100 for g in range(36)], 50, 512, 256, "bf16"),
+    ([17 + (g * 37) % 100 for g in range(31)] + [3, 0], 0, 512, 256, "bf16"),
 ]
 
 
