@@ -37,6 +37,50 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def dump_inputs(cid: int, out_dir: str):
+    """Write what decides the work of a workload (for the native probe that
+    hardware-counter runs use): the tokens, router and bias of a layer
+    (routing depends on nothing else), or the group sizes of the pre-routed
+    grouped workload.  Expert weights are not written: their values do not
+    change which bytes the kernels move."""
+    os.makedirs(out_dir, exist_ok=True)
+    meta = {}
+    if cid == 4:
+        wl = synth.config(4, device="cpu")
+        meta.update(kind="grouped", H=wl.H, I=wl.I, dt=wl.w_dt, shared_rows=wl.shared_m,
+                    groups=" ".join(str(m) for m in wl.group_m))
+    else:
+        wl = synth.routing_inputs(cid)
+        meta.update(kind="layer", T=wl["T"], H=wl["H"], E=wl["E"], k=wl["k"], I=wl["I"], x_dt=wl["x_dt"],
+                    w_dt=wl["w_dt"], out_dt=wl["out_dt"], score=wl["score"], shared=int(wl["shared"]),
+                    bias=int(wl["bias"] is not None))
+        wl["x"].contiguous().view(torch.uint8).numpy().tofile(os.path.join(out_dir, "x.bin"))
+        wl["w_router"].contiguous().numpy().tofile(os.path.join(out_dir, "w_router.bin"))
+        if wl["bias"] is not None:
+            wl["bias"].contiguous().numpy().tofile(os.path.join(out_dir, "bias.bin"))
+    with open(os.path.join(out_dir, "meta.txt"), "w") as f:
+        for k, v in meta.items():
+            f.write(f"{k} {v}\n")
+    log(f"config {cid} inputs written to {out_dir}")
+
+
+def measured_traffic(name: str):
+    """HBM bytes per grouped-FFN call from the stored counter runs
+    (profiles/traffic.json, written by routed_expert_ffn_04_amd.traffic),
+    or None when there is no record for this workload or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != accounting.sources_digest():
+        return None
+    w = rec.get("workloads", {}).get(name)
+    return None if w is None else int(w["bytes"])
+
+
 def build_inputs(cid: int, dev):
     t0 = time.time()
     wl = synth.config(cid, device=dev)
@@ -187,7 +231,11 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the T=128 decode batch)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=8, help="tokens (rows) in the CPU oracle sample")
+    ap.add_argument("--dump-inputs", metavar="DIR", help="write the workload's routing inputs for the native probe and exit")
     args = ap.parse_args()
+    if args.dump_inputs:
+        dump_inputs(args.config, args.dump_inputs)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1", file=sys.stderr)
@@ -227,6 +275,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_TFLOPS[wl.w_dt], "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_TFLOPS[wl.w_dt], 4), "traffic": None}
+    roof["traffic"] = measured_traffic(wl.name)
     roof["kernel"] = "moe_grouped_ffn (tile list + gate/up + down kernels)"
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops

@@ -44,3 +44,23 @@ def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w
     h_row = I * eb[w_dt] + (I // 128 * 4 if w_dt == "e4m3" else 0)
     b += rows * (a_row + 2 * h_row + H * eb[y_dt])
     return b
+
+
+def sources_digest() -> str:
+    """sha256 over the library's kernel and ABI sources (csrc/, include/),
+    in name order: the key that ties a stored traffic measurement to the
+    kernels it was taken on."""
+    import hashlib
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    h = hashlib.sha256()
+    for d in (os.path.join(here, "csrc"), os.path.join(root, "include")):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(name.encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+

@@ -5,6 +5,11 @@
 //   moe_probe skew    [iters]   T=4096,  same layer, additive logit bias on 20 experts
 //   moe_probe prefill [iters]   T=16384, same layer with e4m3 block-scaled weights, bf16 out
 //   moe_probe copy    [iters]   a plain device copy of 1 GiB (counter calibration)
+//   moe_probe file DIR [iters]  the workload described by DIR/meta.txt (written by
+//                               bench.py --dump-inputs): a layer with the dumped
+//                               tokens, router and bias (so its routing is the
+//                               benchmark's), or the pre-routed grouped FFN with
+//                               the dumped group sizes
 //
 // Inputs are filled on the device from a hash of the element index (uniform
 // values with the layer's scales); values matter here only through the
@@ -13,6 +18,9 @@
 
 #include <chrono>
 #include <cstdio>
+#include <fstream>
+#include <map>
+#include <sstream>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -90,7 +98,7 @@ struct BankBuf {
 static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
     BankBuf b{};
     const size_t ne = (size_t)n * H * I;
-    const size_t eb = dt == MOE_E4M3 ? 1 : 2;
+    const size_t eb = dt == MOE_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
     void* g = dalloc(ne * eb);
     void* u = dalloc(ne * eb);
     void* w = dalloc(ne * eb);
@@ -104,6 +112,11 @@ static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
         float* sd = (float*)dalloc(ns * 4);
         for (float* s : {sg, su, sd}) hipLaunchKernelGGL(fill_f32, dim3(256), dim3(256), 0, 0, s, ns, seed + 7, 1e-3f);
         b.d.s_gate = sg; b.d.s_up = su; b.d.s_down = sd;
+    } else if (dt == MOE_F32) {
+        const float a = 0.0346f;
+        hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, (float*)g, ne, seed + 1, a);
+        hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, (float*)u, ne, seed + 2, a);
+        hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, (float*)w, ne, seed + 3, a);
     } else {
         const float a = 0.0346f;   // uniform with standard deviation 0.02
         hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)g, ne, seed + 1, a);
@@ -115,9 +128,40 @@ static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
     return b;
 }
 
+static std::map<std::string, std::string> read_meta(const std::string& dir) {
+    std::map<std::string, std::string> m;
+    std::ifstream f(dir + "/meta.txt");
+    if (!f) {
+        fprintf(stderr, "cannot read %s/meta.txt\n", dir.c_str());
+        exit(1);
+    }
+    std::string line;
+    while (std::getline(f, line)) {
+        const size_t sp = line.find(' ');
+        if (sp != std::string::npos) m[line.substr(0, sp)] = line.substr(sp + 1);
+    }
+    return m;
+}
+
+static void* load_file(const std::string& path, size_t bytes) {
+    std::vector<char> h(bytes);
+    FILE* f = fopen(path.c_str(), "rb");
+    if (!f || fread(h.data(), 1, bytes, f) != bytes) {
+        fprintf(stderr, "cannot read %zu bytes from %s\n", bytes, path.c_str());
+        exit(1);
+    }
+    fclose(f);
+    void* d = dalloc(bytes);
+    CK(hipMemcpy(d, h.data(), bytes, hipMemcpyHostToDevice));
+    return d;
+}
+
+static int dt_of(const std::string& s) { return s == "f32" ? MOE_F32 : s == "bf16" ? MOE_BF16 : MOE_E4M3; }
+
 int main(int argc, char** argv) {
     const std::string mode = argc > 1 ? argv[1] : "decode";
-    const int iters = argc > 2 ? atoi(argv[2]) : 5;
+    const std::string dir = (mode == "file" && argc > 2) ? argv[2] : "";
+    const int iters = mode == "file" ? (argc > 3 ? atoi(argv[3]) : 5) : (argc > 2 ? atoi(argv[2]) : 5);
     hipStream_t st;
     CK(hipStreamCreate(&st));
     hipEvent_t e0, e1;
@@ -142,34 +186,88 @@ int main(int argc, char** argv) {
         return 0;
     }
 
+    if (mode == "file") {
+        auto m = read_meta(dir);
+        if (m["kind"] == "grouped") {
+            const int H = std::stoi(m["H"]), I = std::stoi(m["I"]), S = std::stoi(m["shared_rows"]);
+            const int dt = dt_of(m["dt"]);
+            std::vector<int> offs{0};
+            std::istringstream gs(m["groups"]);
+            for (int g; gs >> g;) offs.push_back(offs.back() + g);
+            const int G = (int)offs.size() - 1, R = offs.back();
+            const size_t eb = dt == MOE_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
+            void* a = dalloc((size_t)(R + S) * H * eb);
+            float* as = (float*)dalloc((size_t)(R + S) * (H / 128) * 4);
+            if (dt == MOE_E4M3) hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)a, (size_t)(R + S) * H, 21);
+            else hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)a, (size_t)(R + S) * H, 21, 1.73f);
+            hipLaunchKernelGGL(fill_f32, dim3(256), dim3(256), 0, 0, as, (size_t)(R + S) * (H / 128), 22, 1e-2f);
+            int32_t* d_offs = (int32_t*)dalloc(offs.size() * 4);
+            CK(hipMemcpy(d_offs, offs.data(), offs.size() * 4, hipMemcpyHostToDevice));
+            BankBuf routed = make_bank(G, H, I, dt, 100);
+            BankBuf shared = make_bank(1, H, I, dt, 200);
+            void* y = dalloc((size_t)R * H * 2);
+            void* y_sh = dalloc((size_t)(S > 0 ? S : 1) * H * 2);
+            const size_t wsb = moe_grouped_ffn_workspace_size(R, G, S, H, I, dt);
+            void* ws = dalloc(wsb);
+            CK(hipDeviceSynchronize());
+            auto run = [&]() {
+                CM(moe_grouped_ffn(a, dt, dt == MOE_E4M3 ? as : nullptr, nullptr, 1, d_offs, G, R, &routed.d,
+                                   S > 0 ? (const uint8_t*)a + (size_t)R * H * eb : nullptr,
+                                   (S > 0 && dt == MOE_E4M3) ? as + (size_t)R * (H / 128) : nullptr, S,
+                                   S > 0 ? &shared.d : nullptr, y, S > 0 ? y_sh : nullptr, MOE_BF16, ws, wsb, st));
+            };
+            run();
+            CK(hipEventRecord(e0, st));
+            for (int i = 0; i < iters; ++i) run();
+            CK(hipEventRecord(e1, st));
+            CK(hipEventSynchronize(e1));
+            float ms = 0;
+            CK(hipEventElapsedTime(&ms, e0, e1));
+            printf("file %s: grouped G=%d R=%d S=%d %.3f ms/call\n", dir.c_str(), G, R, S, ms / iters);
+            return 0;
+        }
+    }
+
     int T, x_dt = MOE_BF16, w_dt, out_dt;
     bool bias = false;
     if (mode == "decode") { T = 128; w_dt = MOE_BF16; out_dt = MOE_F32; }
     else if (mode == "skew") { T = 4096; w_dt = MOE_BF16; out_dt = MOE_F32; bias = true; }
     else if (mode == "prefill") { T = 16384; w_dt = MOE_E4M3; out_dt = MOE_BF16; }
-    else { fprintf(stderr, "unknown mode %s\n", mode.c_str()); return 1; }
-    const int H = 7168, E = 256, k = 8, I = 2048;
-
-    void* x = dalloc((size_t)T * H * 2);
-    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)x, (size_t)T * H, 11, 1.73f);
-    float* wr = (float*)dalloc((size_t)H * E * 4);
-    hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, wr, (size_t)H * E, 12, 1.73f / 84.7f);
+    else if (mode != "file") { fprintf(stderr, "unknown mode %s\n", mode.c_str()); return 1; }
+    int H = 7168, E = 256, k = 8, I = 2048, score = MOE_SIGMOID, has_shared = 1;
+    void* x = nullptr;
+    float* wr = nullptr;
     float* b = nullptr;
-    if (bias) {
-        std::vector<float> hb(E, -1.0f);
-        for (int e = 0; e < 20; ++e) hb[(e * 37) % E] = 2.5f;   // 20 hot experts
-        b = (float*)dalloc(E * 4);
-        CK(hipMemcpy(b, hb.data(), E * 4, hipMemcpyHostToDevice));
+    if (mode == "file") {
+        auto m = read_meta(dir);
+        T = std::stoi(m["T"]); H = std::stoi(m["H"]); E = std::stoi(m["E"]); k = std::stoi(m["k"]); I = std::stoi(m["I"]);
+        x_dt = dt_of(m["x_dt"]); w_dt = dt_of(m["w_dt"]); out_dt = dt_of(m["out_dt"]);
+        score = m["score"] == "softmax" ? MOE_SOFTMAX : MOE_SIGMOID;
+        has_shared = std::stoi(m["shared"]);
+        x = load_file(dir + "/x.bin", (size_t)T * H * (x_dt == MOE_F32 ? 4 : 2));
+        wr = (float*)load_file(dir + "/w_router.bin", (size_t)H * E * 4);
+        if (std::stoi(m["bias"])) b = (float*)load_file(dir + "/bias.bin", (size_t)E * 4);
+    } else {
+        x = dalloc((size_t)T * H * 2);
+        hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)x, (size_t)T * H, 11, 1.73f);
+        wr = (float*)dalloc((size_t)H * E * 4);
+        hipLaunchKernelGGL(fill_f32, dim3(4096), dim3(256), 0, 0, wr, (size_t)H * E, 12, 1.73f / 84.7f);
+        if (bias) {
+            std::vector<float> hb(E, -1.0f);
+            for (int e = 0; e < 20; ++e) hb[(e * 37) % E] = 2.5f;   // 20 hot experts
+            b = (float*)dalloc(E * 4);
+            CK(hipMemcpy(b, hb.data(), E * 4, hipMemcpyHostToDevice));
+        }
     }
     BankBuf routed = make_bank(E, H, I, w_dt, 100);
     BankBuf shared = make_bank(1, H, I, w_dt, 200);
     void* out = dalloc((size_t)T * H * (out_dt == MOE_BF16 ? 2 : 4));
-    const size_t wsb = moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, 1, out_dt);
+    const size_t wsb = moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt);
     void* ws = dalloc(wsb);
     CK(hipDeviceSynchronize());
 
     auto run = [&]() {
-        CM(moe_layer(x, x_dt, T, H, wr, b, E, k, MOE_SIGMOID, &routed.d, &shared.d, out, out_dt, nullptr,
+        CM(moe_layer(x, x_dt, T, H, wr, b, E, k, score, &routed.d, has_shared ? &shared.d : nullptr, out, out_dt, nullptr,
                      nullptr, nullptr, ws, wsb, st));
     };
     run();

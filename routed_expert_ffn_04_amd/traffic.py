@@ -1,0 +1,125 @@
+"""Measured HBM traffic of the grouped FFN per call, for the benchmark's
+roofline record.
+
+Run on a machine with the GPU (the parent process never touches it):
+
+    python -m routed_expert_ffn_04_amd.traffic --configs 2 5
+
+For every workload it writes the routing inputs (bench.py --dump-inputs),
+then runs the native probe (no torch) on exactly that routing under two
+rocprofv3 counter passes, FETCH_SIZE and WRITE_SIZE, and sums the counters of
+the grouped-FFN kernels per call.  The counters are scaled by what they read
+for a plain device copy of 1 GiB (probe mode "copy"), so the figures are
+bytes.  The result goes to profiles/traffic.json together with a digest of
+the kernel sources; bench.py reports the figure only while the sources still
+match that digest.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+from routed_expert_ffn_04_amd.accounting import sources_digest  # noqa: E402
+
+PROBE = os.path.join(HERE, "moe_probe")
+GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::gffn_build_lists")
+NAMES = {
+    1: "tiny-fp32-T64-H256-E8-top2",
+    2: "dsv3-decode-bf16-T128-H7168-E256+1-top8",
+    3: "dsv3-skew-bf16-T4096-H7168-E256+1-top8-zipf1.2",
+    4: "ep-prefill-share-fp8-9+1groups-H7168-I2048",
+    5: "dsv3-prefill-fp8-T16384-H7168-E256+1-top8",
+}
+
+
+def run(cmd, log):
+    with open(log, "w") as f:
+        r = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, timeout=300)
+    if r.returncode != 0:
+        with open(log) as f:
+            tail = f.read()[-2000:]
+        raise RuntimeError(f"{' '.join(cmd)} failed ({r.returncode}):\n{tail}")
+
+
+def counter_sums(out_dir):
+    """{kernel name: [per-dispatch counter values]} of one pass."""
+    files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise RuntimeError(f"no counter file under {out_dir}")
+    per = {}
+    for fn in files:
+        for r in csv.DictReader(open(fn)):
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def pmc_pass(counter, probe_args, work, tag):
+    out = os.path.join(work, f"{tag}_{counter}")
+    shutil.rmtree(out, ignore_errors=True)
+    cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--", PROBE, *probe_args]
+    run(["timeout", "-s", "KILL", "120", *cmd], out + ".log")
+    return counter_sums(out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--configs", type=int, nargs="+", default=[2, 5])
+    ap.add_argument("--calls", type=int, default=2, help="timed calls per probe run (one more is the warm-up)")
+    ap.add_argument("--work", default="/tmp/moe_traffic", help="scratch (dumped inputs, raw counter files)")
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    args = ap.parse_args()
+    os.makedirs(args.work, exist_ok=True)
+    os.environ.setdefault("TMPDIR", "/tmp")
+
+    # calibration: a 1 GiB device copy (probe: one untimed + `calls` timed copies)
+    gib = float(1 << 30)
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = pmc_pass(counter, ["copy", str(args.calls)], args.work, "copy")
+        vals = [v for k, v in per.items() if "copy_u4" in k][0]
+        kib = sum(vals) / len(vals)
+        cal[counter] = {"kib_per_gib_copy": kib, "bytes_per_kib": gib / kib}
+        print(f"calibration {counter}: {kib:.0f} KiB per 1 GiB copy -> {gib / kib:.1f} bytes per KiB", flush=True)
+
+    result = {"sources_sha256": sources_digest(), "calibration": cal, "workloads": {}}
+    for cid in args.configs:
+        d = os.path.join(args.work, f"inputs_c{cid}")
+        run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(cid), "--dump-inputs", d],
+            os.path.join(args.work, f"dump_c{cid}.log"))
+        ncalls = args.calls + 1
+        rec = {"calls": ncalls, "kernels": {}}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            per = pmc_pass(counter, ["file", d, str(args.calls)], args.work, f"c{cid}")
+            tot = 0.0
+            for k, vals in per.items():
+                if not any(s in k for s in GFFN_KERNELS):
+                    continue
+                b = sum(vals) / ncalls * cal[counter]["bytes_per_kib"]
+                rec["kernels"].setdefault(k, {})[counter] = round(b)
+                tot += b
+            rec[counter.lower().replace("_size", "_bytes")] = round(tot)
+        rec["bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+        rec["command"] = (f"python -m routed_expert_ffn_04_amd.traffic --configs {' '.join(map(str, args.configs))}"
+                          f" (probe: moe_probe file <dump of bench.py --config {cid}> {args.calls})")
+        result["workloads"][NAMES[cid]] = rec
+        print(f"config {cid}: grouped FFN per call: fetch {rec['fetch_bytes'] / 1e9:.3f} GB, "
+              f"write {rec['write_bytes'] / 1e9:.3f} GB", flush=True)
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    with open(args.out, "w") as f:
+        json.dump(result, f, indent=1)
+    print(f"wrote {args.out}")
+
+
+if __name__ == "__main__":
+    main()

@@ -310,6 +310,34 @@ def make_grouped(group_m, shared_m, H, I, *, dt="e4m3", seed=4, device="cpu", w_
     return wl
 
 
+def routing_inputs(cid: int, device="cpu") -> dict:
+    """The draws of layer workload cid that decide its routing (tokens,
+    router, bias) and its shape, without the expert banks: the same values
+    config(cid) holds."""
+    if cid == 1:
+        T, H, E, k, I, seed_l, seed_x = 64, 256, 8, 2, 512, 1, 1
+        shape = dict(x_dt="f32", w_dt="f32", out_dt="f32", score="softmax", shared=False)
+        bias = None
+    elif cid == 2:
+        T, H, E, k, I, seed_l, seed_x = 128, 7168, 256, 8, 2048, 2, 2
+        shape = dict(x_dt="bf16", w_dt="bf16", out_dt="f32", score="sigmoid", shared=True)
+        bias = None
+    elif cid == 3:
+        T, H, E, k, I, seed_l, seed_x = 4096, 7168, 256, 8, 2048, 2, 3
+        shape = dict(x_dt="bf16", w_dt="bf16", out_dt="f32", score="sigmoid", shared=True)
+        bias, _ = zipf_bias(256, 8, 1.2, seed=3)
+    elif cid == 5:
+        T, H, E, k, I, seed_l, seed_x = 16384, 7168, 256, 8, 2048, 2, 5
+        shape = dict(x_dt="bf16", w_dt="e4m3", out_dt="bf16", score="sigmoid", shared=True)
+        bias = None
+    else:
+        raise ValueError(cid)
+    xdt = torch.float32 if shape["x_dt"] == "f32" else torch.bfloat16
+    x = normal((T, H), seed_x, ST_X, 1.0, xdt, device)
+    wr = normal((H, E), seed_l, ST_ROUTER, 1.0 / math.sqrt(H), torch.float32, device)
+    return dict(T=T, H=H, E=E, k=k, I=I, x=x, w_router=wr, bias=None if bias is None else bias.to(device), **shape)
+
+
 def config(cid: int, device="cpu", T: Optional[int] = None) -> Workload:
     """The five seeded workloads.  `T` overrides the token count (the layer
     and every other draw stay the same), for sampled or shrunken runs."""
