@@ -155,6 +155,9 @@ GROUPED_CASES = [
     # the weight-streaming tiles to the 256-row tiles (and 31: just too few)
     ([17 + (g * 37) % 100 for g in range(36)], 50, 512, 256, "bf16"),
     ([17 + (g * 37) % 100 for g in range(31)] + [3, 0], 0, 512, 256, "bf16"),
+    # m-tile boundaries of the 256-row tiles: exact multiples, one short, one over
+    ([256, 512, 255, 257, 1], 256, 512, 256, "e4m3"),
+    ([256, 512, 255, 257, 1], 0, 512, 256, "bf16"),
 ]
 
 
