@@ -37,7 +37,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def dump_inputs(cid: int, out_dir: str):
+def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False):
     """Write what decides the work of a workload (for the native probe that
     hardware-counter runs use): the tokens, router and bias of a layer
     (routing depends on nothing else), or the group sizes of the pre-routed
@@ -54,6 +54,8 @@ def dump_inputs(cid: int, out_dir: str):
         meta.update(kind="layer", T=wl["T"], H=wl["H"], E=wl["E"], k=wl["k"], I=wl["I"], x_dt=wl["x_dt"],
                     w_dt=wl["w_dt"], out_dt=wl["out_dt"], score=wl["score"], shared=int(wl["shared"]),
                     bias=int(wl["bias"] is not None))
+        if fp8_combine:
+            meta["y_dt"] = "e4m3"
         wl["x"].contiguous().view(torch.uint8).numpy().tofile(os.path.join(out_dir, "x.bin"))
         wl["w_router"].contiguous().numpy().tofile(os.path.join(out_dir, "w_router.bin"))
         if wl["bias"] is not None:
@@ -92,9 +94,10 @@ def build_inputs(cid: int, dev):
 class LayerRunner:
     """The layer as its five C-ABI calls with preallocated buffers."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, fp8_combine: bool = False):
         self.wl = wl
         T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
+        self.fp8_combine = fp8_combine
         self.routed = moe.Experts.from_bank(wl.routed)
         self.shared = moe.Experts.from_bank(wl.shared) if wl.shared is not None else None
         self.fp8 = wl.w_dt == "e4m3"
@@ -113,7 +116,8 @@ class LayerRunner:
         self.dest = torch.empty(R, dtype=torch.int32, device=dev)
         self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.fp8 else None
         self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
-        self.y = torch.empty((R, H), dtype=ydt, device=dev)
+        self.y = torch.empty((R, H), dtype=torch.uint8 if fp8_combine else ydt, device=dev)
+        self.y_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8_combine else None
         self.y_sh = torch.empty((T, H), dtype=ydt, device=dev) if self.shared else None
         self.out = torch.empty((T, H), dtype=ydt, device=dev)
         self.names = ["route", "quant", "permute", "grouped_ffn", "combine"] if self.fp8 else \
@@ -131,8 +135,8 @@ class LayerRunner:
         yield "grouped_ffn", lambda: moe.grouped_ffn(
             a, self.offsets, self.routed, a_scale=a_s, src=self.src, src_div=wl.k, R_max=wl.T * wl.k,
             a_sh=a if self.shared else None, a_sh_scale=a_s if self.shared else None, shared=self.shared,
-            y=self.y, y_sh=self.y_sh, ws=self.ws_ffn)
-        yield "combine", lambda: moe.combine(self.y, self.y_sh, self.dest, self.w, out=self.out)
+            y=self.y, y_scale=self.y_scale, y_sh=self.y_sh, ws=self.ws_ffn)
+        yield "combine", lambda: moe.combine(self.y, self.y_sh, self.dest, self.w, out=self.out, y_scale=self.y_scale)
 
 
 class GroupedRunner:
@@ -252,9 +256,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=16, help="tokens (rows) in the CPU oracle sample")
     ap.add_argument("--dump-inputs", metavar="DIR", help="write the workload's routing inputs for the native probe and exit")
+    ap.add_argument("--fp8-combine", action="store_true",
+                    help="routed expert outputs as e4m3 per 1x128 before the combine (fp8 layers)")
     args = ap.parse_args()
     if args.dump_inputs:
-        dump_inputs(args.config, args.dump_inputs)
+        dump_inputs(args.config, args.dump_inputs, args.fp8_combine)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -267,7 +273,12 @@ def main():
     dev = torch.device("cuda:0")
     cid = args.config
     wl = build_inputs(cid, dev)
-    runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev)
+    if args.fp8_combine and (cid == 4 or wl.w_dt != "e4m3"):
+        print("bench.py: --fp8-combine applies to the fp8 layer workloads only", file=sys.stderr)
+        sys.exit(2)
+    if args.fp8_combine:
+        wl.y_dt = "e4m3"          # also what the CPU oracle baseline computes
+    runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev, fp8_combine=args.fp8_combine)
     ms, per, wall = run_timed(runner, args.steps, args.warmup)
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; per call (ms): " +
         ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
@@ -284,7 +295,8 @@ def main():
         y_dt = wl.out_dt
     rows = sum(group_rows) + shared_rows
     flops = accounting.ffn_flops(rows, wl.H, wl.I)
-    nbytes = accounting.grouped_ffn_bytes(group_rows, shared_rows, wl.H, wl.I, a_dt, wl.w_dt, y_dt)
+    nbytes = accounting.grouped_ffn_bytes(group_rows, shared_rows, wl.H, wl.I, a_dt, wl.w_dt,
+                                          "e4m3" if args.fp8_combine else y_dt, y_dt)
     gffn_ms = per["grouped_ffn"]
     gbs = nbytes / (gffn_ms * 1e-3) / 1e9
     tfs = flops / (gffn_ms * 1e-3) / 1e12
@@ -295,7 +307,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_TFLOPS[wl.w_dt], "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_TFLOPS[wl.w_dt], 4), "traffic": None}
-    roof["traffic"] = measured_traffic(wl.name)
+    roof["traffic"] = measured_traffic(wl.name + ("+fp8-combine" if args.fp8_combine else ""))
     roof["kernel"] = "moe_grouped_ffn (tile list + gate/up + down kernels)"
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -311,6 +323,7 @@ def main():
     else:
         cfg.update(T=wl.T, E=wl.E, k=wl.k, shared=int(wl.shared is not None), score=wl.score,
                    bias="zipf1.2" if wl.bias is not None else None, x=wl.x_dt, out=wl.out_dt,
+                   y="e4m3 (fp8 combine)" if args.fp8_combine else wl.out_dt,
                    experts_touched=sum(1 for c in group_rows if c > 0))
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,

@@ -137,7 +137,11 @@ moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int
  * E4M3 activations carry a_scale [rows of a][H/128] (a_sh_scale likewise).
  * offsets: [G+1] int32 device array with offsets[0] = 0 and
  * offsets[G] <= R_max (R_max, a host value, bounds the routed rows and sizes
- * the launch).  y: [R_max][H], y_sh: [S][H], both of type y_dt (F32 or BF16).
+ * the launch).  y: [R_max][H] of type y_dt: F32, BF16, or E4M3 = codes
+ * quantised per row and 128-column block exactly as in moe_quant_e4m3_1x128
+ * (from the fp32 accumulators) with the scales in y_scale [R_max][H/128]
+ * (E4M3 y needs E4M3 weights and H a multiple of 256; y_scale is ignored
+ * otherwise).  y_sh: [S][H] of type y_sh_dt (F32 or BF16).
  * routed->n must equal G; H, I multiples of 128. */
 moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale,
                              const int32_t* src, int32_t src_div,
@@ -145,7 +149,7 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale,
                              const moe_experts_t* routed,
                              const void* a_sh, const float* a_sh_scale, int32_t S,
                              const moe_experts_t* shared,
-                             void* y, void* y_sh, int32_t y_dt,
+                             void* y, int32_t y_dt, float* y_scale, void* y_sh, int32_t y_sh_dt,
                              void* ws, size_t ws_bytes, void* stream);
 size_t moe_grouped_ffn_workspace_size(int32_t R_max, int32_t G, int32_t S, int32_t H,
                                       int32_t I, int32_t w_dt);
@@ -153,8 +157,12 @@ size_t moe_grouped_ffn_workspace_size(int32_t R_max, int32_t G, int32_t S, int32
 /* ---- combine ------------------------------------------------------------
  * out[t] = y_sh[t] + sum_{j=0}^{k-1} topk_w[t][j] * y_perm[dest[t*k+j]]
  * accumulated in fp32 in this order (y_sh = 0 when NULL), then rounded to
- * out_dt (F32 or BF16).  y_perm: [T*k][H], y_sh: [T][H], both y_dt. */
-moe_status_t moe_combine(const void* y_perm, const void* y_sh, int32_t y_dt,
+ * out_dt (F32 or BF16).  y_perm: [T*k][H] of type y_dt (F32, BF16, or E4M3
+ * codes whose value is code * y_scale[row][col/128], y_scale [T*k][H/128]:
+ * the FP8 combine of "DeepSeek V3/R1 Inference Efficiency (2)", section 2);
+ * y_sh: [T][H] of type y_sh_dt (F32 or BF16). */
+moe_status_t moe_combine(const void* y_perm, int32_t y_dt, const float* y_scale,
+                         const void* y_sh, int32_t y_sh_dt,
                          const int32_t* dest, const float* topk_w, int32_t T, int32_t k,
                          int32_t H, void* out, int32_t out_dt, void* stream);
 
@@ -162,17 +170,20 @@ moe_status_t moe_combine(const void* y_perm, const void* y_sh, int32_t y_dt,
  * route -> (E4M3 weights: quantise x once per token) -> permute -> grouped
  * FFN over the routed groups and the shared expert -> combine, all enqueued
  * on `stream`.  Supported: x F32 with F32 weights; x BF16 with BF16 or E4M3
- * weights.  y_perm/y_sh are kept in fp32 when out_dt is F32 and in bf16 when
- * out_dt is BF16.  topk_ids_out [T][k], topk_w_out [T][k], counts_out [E] are
- * optional copies of the routing results (NULL to skip). */
+ * weights.  y_sh is kept in fp32 when out_dt is F32 and in bf16 when out_dt
+ * is BF16; the routed expert outputs y_perm in y_dt: F32 or BF16, or E4M3
+ * (the FP8 combine; E4M3 weights and H a multiple of 256 only).
+ * topk_ids_out [T][k], topk_w_out [T][k], counts_out [E] are optional copies
+ * of the routing results (NULL to skip). */
 moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H,
                        const float* w_router, const float* bias, int32_t E, int32_t k,
                        int32_t score, const moe_experts_t* routed, const moe_experts_t* shared,
-                       void* out, int32_t out_dt,
+                       void* out, int32_t out_dt, int32_t y_dt,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                        void* ws, size_t ws_bytes, void* stream);
 size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, int32_t I,
-                                int32_t x_dt, int32_t w_dt, int32_t has_shared, int32_t out_dt);
+                                int32_t x_dt, int32_t w_dt, int32_t has_shared, int32_t out_dt,
+                                int32_t y_dt);
 
 /* Name of a status code; text of the calling thread's last error ("" if none). */
 const char* moe_status_string(int32_t status);

@@ -63,12 +63,12 @@ def lib() -> ctypes.CDLL:
             "moe_permute_workspace_size": ([_I32, _I32, _I32], _SZ),
             "moe_quant_e4m3_1x128": ([_P, _I32, _I32, _I32, _P, _P, _P], _I32),
             "moe_grouped_ffn": ([_P, _I32, _P, _P, _I32, _P, _I32, _I32, ctypes.POINTER(ExpertsT),
-                                 _P, _P, _I32, ctypes.POINTER(ExpertsT), _P, _P, _I32, _P, _SZ, _P], _I32),
+                                 _P, _P, _I32, ctypes.POINTER(ExpertsT), _P, _I32, _P, _P, _I32, _P, _SZ, _P], _I32),
             "moe_grouped_ffn_workspace_size": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
-            "moe_combine": ([_P, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _I32, _P], _I32),
+            "moe_combine": ([_P, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _I32, _P], _I32),
             "moe_layer": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(ExpertsT),
-                           ctypes.POINTER(ExpertsT), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
-            "moe_layer_workspace_size": ([_I32] * 9, _SZ),
+                           ctypes.POINTER(ExpertsT), _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+            "moe_layer_workspace_size": ([_I32] * 10, _SZ),
             "moe_status_string": ([_I32], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -190,50 +190,67 @@ def quant_e4m3_1x128(x, stream=None, out=None):
     return q, s
 
 
+def _is_fp8(dtype) -> bool:
+    import torch
+    return dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
 def grouped_ffn(a, offsets, routed: Experts, *, a_scale=None, src=None, src_div: int = 1, R_max=None,
                 a_sh=None, a_sh_scale=None, shared: Optional[Experts] = None, y_dtype=None,
-                y=None, y_sh=None, stream=None, ws=None):
-    """y [R_max][H], y_sh [S][H] (moe_grouped_ffn)."""
+                y=None, y_scale=None, y_sh=None, y_sh_dtype=None, stream=None, ws=None):
+    """moe_grouped_ffn.  Returns (y [R_max][H], y_sh [S][H]); with an fp8 y_dtype
+    (torch.uint8 codes) y is the pair (codes, scales [R_max][H/128])."""
     import torch
     rs = routed.struct()
     G, H = rs.n, rs.H
     R_max = (src.numel() if src is not None else a.shape[0]) if R_max is None else R_max
     S = 0 if a_sh is None else a_sh.shape[0]
     ss = shared.struct() if shared is not None else None
-    y_dtype = y_dtype or torch.float32
+    y_dtype = y.dtype if y is not None else (y_dtype or torch.float32)
+    fp8_y = _is_fp8(y_dtype)
+    y_sh_dtype = y_sh_dtype or (torch.bfloat16 if fp8_y else y_dtype)
     dev = a.device
     if y is None:
-        y = torch.empty((R_max, H), dtype=y_dtype, device=dev)
+        y = torch.empty((R_max, H), dtype=torch.uint8 if fp8_y else y_dtype, device=dev)
+    if fp8_y and y_scale is None:
+        y_scale = torch.empty((R_max, H // 128), dtype=torch.float32, device=dev)
     if y_sh is None and shared is not None and S > 0:
-        y_sh = torch.empty((S, H), dtype=y_dtype, device=dev)
+        y_sh = torch.empty((S, H), dtype=y_sh_dtype, device=dev)
     need = lib().moe_grouped_ffn_workspace_size(R_max, G, S if shared is not None else 0, H, rs.I, rs.dt)
     ws = ws if ws is not None else _workspace(need, dev)
     _check(lib().moe_grouped_ffn(_ptr(a), _dt_of(a), _ptr(a_scale), _ptr(src), src_div, _ptr(offsets), G, R_max,
                                  ctypes.byref(rs), _ptr(a_sh), _ptr(a_sh_scale), S,
                                  ctypes.byref(ss) if ss is not None else None,
-                                 _ptr(y), _ptr(y_sh), _dt_of(y), _ptr(ws), ws.numel(), _stream(stream)))
-    return y, y_sh
+                                 _ptr(y), _dt_of(y), _ptr(y_scale) if fp8_y else None, _ptr(y_sh),
+                                 _dt_of(y_sh) if y_sh is not None else F32, _ptr(ws), ws.numel(), _stream(stream)))
+    return ((y, y_scale) if fp8_y else y), y_sh
 
 
-def combine(y_perm, y_sh, dest, topk_w, out_dtype=None, out=None, stream=None):
+def combine(y_perm, y_sh, dest, topk_w, out_dtype=None, out=None, stream=None, y_scale=None):
+    """moe_combine.  y_perm fp32/bf16, or e4m3 codes (torch.uint8) with
+    y_scale [rows][H/128]."""
     import torch
     T, k = topk_w.shape
     H = y_perm.shape[1]
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
-    _check(lib().moe_combine(_ptr(y_perm), _ptr(y_sh), _dt_of(y_perm), _ptr(dest), _ptr(topk_w), T, k, H,
+    _check(lib().moe_combine(_ptr(y_perm), _dt_of(y_perm), _ptr(y_scale), _ptr(y_sh),
+                             _dt_of(y_sh) if y_sh is not None else F32, _ptr(dest), _ptr(topk_w), T, k, H,
                              _ptr(out), _dt_of(out), _stream(stream)))
     return out
 
 
-def layer_workspace_size(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt) -> int:
-    return lib().moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, int(has_shared), out_dt)
+def layer_workspace_size(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt, y_dt=None) -> int:
+    return lib().moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, int(has_shared), out_dt,
+                                          out_dt if y_dt is None else y_dt)
 
 
 def layer(x, w_router, bias, k: int, score: str, routed: Experts, shared: Optional[Experts] = None,
-          out_dtype=None, out=None, want_routing: bool = False, ws=None, stream=None):
-    """The fused layer (moe_layer).  Returns out, or (out, ids, w, counts)."""
+          out_dtype=None, out=None, want_routing: bool = False, ws=None, stream=None, y_dtype=None):
+    """The fused layer (moe_layer).  Returns out, or (out, ids, w, counts).
+    y_dtype: dtype of the routed expert outputs before the combine (default:
+    out_dtype; torch.uint8 = e4m3, the FP8 combine)."""
     import torch
     T, H = x.shape
     E = w_router.shape[1]
@@ -248,10 +265,11 @@ def layer(x, w_router, bias, k: int, score: str, routed: Experts, shared: Option
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         counts = torch.empty(E, dtype=torch.int32, device=dev)
-    need = layer_workspace_size(T, H, E, k, rs.I, _dt_of(x), rs.dt, ss is not None, _dt_of(out))
+    y_dt = _dt_of(out) if y_dtype is None else (E4M3 if _is_fp8(y_dtype) else _dt_of(torch.empty(0, dtype=y_dtype)))
+    need = layer_workspace_size(T, H, E, k, rs.I, _dt_of(x), rs.dt, ss is not None, _dt_of(out), y_dt)
     ws = ws if ws is not None else _workspace(need, dev)
     _check(lib().moe_layer(_ptr(x), _dt_of(x), T, H, _ptr(w_router), _ptr(bias), E, k, SCORE[score],
                            ctypes.byref(rs), ctypes.byref(ss) if ss is not None else None,
-                           _ptr(out), _dt_of(out), _ptr(ids), _ptr(w), _ptr(counts),
+                           _ptr(out), _dt_of(out), y_dt, _ptr(ids), _ptr(w), _ptr(counts),
                            _ptr(ws), ws.numel(), _stream(stream)))
     return (out, ids, w, counts) if want_routing else out

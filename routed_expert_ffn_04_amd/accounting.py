@@ -33,16 +33,20 @@ def weight_bytes_per_expert(H: int, I: int, w_dt: str) -> int:
     return b
 
 
-def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w_dt: str, y_dt: str) -> int:
+def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w_dt: str, y_dt: str,
+                      y_sh_dt: str = None) -> int:
     """Minimum HBM traffic of one grouped-FFN call.  group_rows: rows per
-    routed group (experts with 0 rows are not read)."""
+    routed group (experts with 0 rows are not read).  y_dt: routed outputs
+    (e4m3 carries a fp32 scale per 128 values); y_sh_dt: shared outputs
+    (default y_dt)."""
     eb = {"f32": 4, "bf16": 2, "e4m3": 1}
+    y_sh_dt = y_sh_dt or y_dt
     touched = sum(1 for m in group_rows if m > 0) + (1 if shared_rows > 0 else 0)
     rows = sum(group_rows) + shared_rows
     b = touched * weight_bytes_per_expert(H, I, w_dt)
-    a_row = H * eb[a_dt] + (H // 128 * 4 if a_dt == "e4m3" else 0)
-    h_row = I * eb[w_dt] + (I // 128 * 4 if w_dt == "e4m3" else 0)
-    b += rows * (a_row + 2 * h_row + H * eb[y_dt])
+    row = lambda n, dt: n * eb[dt] + (n // 128 * 4 if dt == "e4m3" else 0)
+    b += rows * (row(H, a_dt) + 2 * row(I, w_dt))
+    b += sum(group_rows) * row(H, y_dt) + shared_rows * row(H, y_sh_dt)
     return b
 
 

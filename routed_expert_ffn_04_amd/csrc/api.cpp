@@ -146,8 +146,8 @@ size_t moe_grouped_ffn_workspace_size(int32_t R_max, int32_t G, int32_t S, int32
 moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, const int32_t* src,
                              int32_t src_div, const int32_t* offsets, int32_t G, int32_t R_max,
                              const moe_experts_t* routed, const void* a_sh, const float* a_sh_scale,
-                             int32_t S, const moe_experts_t* shared, void* y, void* y_sh, int32_t y_dt,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             int32_t S, const moe_experts_t* shared, void* y, int32_t y_dt, float* y_scale,
+                             void* y_sh, int32_t y_sh_dt, void* ws, size_t ws_bytes, void* stream) {
     if (G < 0 || R_max < 0 || S < 0) return fail(MOE_ERR_INVALID, "grouped_ffn: G=%d R_max=%d S=%d", G, R_max, S);
     if (G > 1024) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: G=%d > 1024", G);
     if (G > 0 && !routed) return fail(MOE_ERR_INVALID, "grouped_ffn: null routed bank");
@@ -162,10 +162,15 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, 
     const int wdt = ref->dt;
     if (shared && shared->dt != wdt) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: shared/routed dtype differ");
     if (a_dt != wdt) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: activation dtype %d with weights %d", a_dt, wdt);
-    if (y_dt != MOE_F32 && y_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y dtype %d", y_dt);
+    if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y dtype %d", y_dt);
+    if (y_dt == MOE_E4M3 && (wdt != MOE_E4M3 || H % 256))
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: E4M3 y needs E4M3 weights and H %% 256 == 0 (H=%d)", H);
+    if (y_sh_dt != MOE_F32 && y_sh_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y_sh dtype %d", y_sh_dt);
     if (src && src_div <= 0) return fail(MOE_ERR_INVALID, "grouped_ffn: src_div=%d", src_div);
     const bool has_sh = shared && S > 0;
     if (R_max > 0 && G > 0 && (!a || !offsets || !y)) return fail(MOE_ERR_INVALID, "grouped_ffn: null a/offsets/y");
+    if (R_max > 0 && G > 0 && y_dt == MOE_E4M3 && !y_scale) return fail(MOE_ERR_INVALID, "grouped_ffn: E4M3 y without y_scale");
     if (has_sh && (!a_sh || !y_sh)) return fail(MOE_ERR_INVALID, "grouped_ffn: null a_sh/y_sh");
     if (wdt == MOE_E4M3 && ((R_max > 0 && G > 0 && !a_scale) || (has_sh && !a_sh_scale)))
         return fail(MOE_ERR_INVALID, "grouped_ffn: E4M3 activations without scales");
@@ -184,22 +189,27 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, 
     p.a_sh = a_sh; p.a_sh_scale = a_sh_scale; p.S = has_sh ? S : 0; p.has_shared = has_sh;
     p.shared = to_bank(shared);
     p.H = H; p.I = I; p.y = y; p.y_sh = y_sh; p.y_bf16 = (y_dt == MOE_BF16);
+    p.y_e4m3 = (y_dt == MOE_E4M3); p.y_scale = y_scale; p.y_sh_bf16 = (y_sh_dt == MOE_BF16);
     return hip_check(moe::launch_gffn(p, ws, (hipStream_t)stream), "moe_grouped_ffn");
 }
 
 // ------------------------------------------------------------------ combine
-moe_status_t moe_combine(const void* y_perm, const void* y_sh, int32_t y_dt, const int32_t* dest,
-                         const float* topk_w, int32_t T, int32_t k, int32_t H, void* out, int32_t out_dt,
-                         void* stream) {
+moe_status_t moe_combine(const void* y_perm, int32_t y_dt, const float* y_scale, const void* y_sh,
+                         int32_t y_sh_dt, const int32_t* dest, const float* topk_w, int32_t T, int32_t k,
+                         int32_t H, void* out, int32_t out_dt, void* stream) {
     if (T < 0 || k <= 0 || H <= 0) return fail(MOE_ERR_INVALID, "combine: T=%d k=%d H=%d", T, k, H);
     if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "combine: H=%d not a multiple of 128", H);
-    if (y_dt != MOE_F32 && y_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "combine: y dtype %d", y_dt);
+    if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "combine: y dtype %d", y_dt);
+    if (y_sh && y_sh_dt != MOE_F32 && y_sh_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "combine: y_sh dtype %d", y_sh_dt);
     if (out_dt != MOE_F32 && out_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "combine: out dtype %d", out_dt);
     if (T == 0) return MOE_OK;
     if (!y_perm || !dest || !topk_w || !out) return fail(MOE_ERR_INVALID, "combine: null pointer");
+    if (y_dt == MOE_E4M3 && !y_scale) return fail(MOE_ERR_INVALID, "combine: E4M3 y without y_scale");
     if (!aligned16(y_perm) || (y_sh && !aligned16(y_sh)) || !aligned16(out))
         return fail(MOE_ERR_INVALID, "combine: misaligned y or out");
-    return hip_check(moe::launch_combine(y_perm, y_sh, y_dt == MOE_BF16, dest, topk_w, T, k, H, out,
+    const int ym = y_dt == MOE_E4M3 ? 2 : y_dt == MOE_BF16 ? 1 : 0;
+    return hip_check(moe::launch_combine(y_perm, ym, y_scale, y_sh, y_sh_dt == MOE_BF16, dest, topk_w, T, k, H, out,
                                          out_dt == MOE_BF16, (hipStream_t)stream),
                      "moe_combine");
 }
@@ -207,14 +217,15 @@ moe_status_t moe_combine(const void* y_perm, const void* y_sh, int32_t y_dt, con
 // ------------------------------------------------------------------ layer
 namespace {
 struct LayerWs {
-    size_t logits, ids, w, counts, offsets, src, dest, perm, xq, xs, yperm, ysh, gffn, total;
+    size_t logits, ids, w, counts, offsets, src, dest, perm, xq, xs, yperm, yscale, ysh, gffn, total;
 };
 
-LayerWs layer_ws(int T, int H, int E, int k, int I, int x_dt, int w_dt, int has_sh, int out_dt) {
+LayerWs layer_ws(int T, int H, int E, int k, int I, int x_dt, int w_dt, int has_sh, int out_dt, int y_dt) {
     (void)x_dt;
     LayerWs L{};
     const size_t R = (size_t)T * k;
-    const size_t yb = out_dt == MOE_BF16 ? 2 : 4;
+    const size_t yb = out_dt == MOE_BF16 ? 2 : 4;                                   // y_sh
+    const size_t ypb = y_dt == MOE_E4M3 ? 1 : y_dt == MOE_BF16 ? 2 : 4;             // y_perm
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += al(bytes); return r; };
     L.logits = take((size_t)T * E * 4);
@@ -227,7 +238,8 @@ LayerWs layer_ws(int T, int H, int E, int k, int I, int x_dt, int w_dt, int has_
     L.perm = take(moe::permute_ws_bytes((int)R, E));
     L.xq = take(w_dt == MOE_E4M3 ? (size_t)T * H : 0);
     L.xs = take(w_dt == MOE_E4M3 ? (size_t)T * (H / 128) * 4 : 0);
-    L.yperm = take(R * H * yb);
+    L.yperm = take(R * H * ypb);
+    L.yscale = take(y_dt == MOE_E4M3 ? R * (H / 128) * 4 : 0);
     L.ysh = take(has_sh ? (size_t)T * H * yb : 0);
     L.gffn = take(moe::gffn_ws_bytes((int)R, E, has_sh ? T : 0, H, I, w_dt));
     L.total = o;
@@ -236,14 +248,14 @@ LayerWs layer_ws(int T, int H, int E, int k, int I, int x_dt, int w_dt, int has_
 }  // namespace
 
 size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, int32_t I, int32_t x_dt,
-                                int32_t w_dt, int32_t has_shared, int32_t out_dt) {
+                                int32_t w_dt, int32_t has_shared, int32_t out_dt, int32_t y_dt) {
     if (T < 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0) return 0;
-    return layer_ws(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt).total;
+    return layer_ws(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt, y_dt).total;
 }
 
 moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const float* w_router,
                        const float* bias, int32_t E, int32_t k, int32_t score, const moe_experts_t* routed,
-                       const moe_experts_t* shared, void* out, int32_t out_dt, int32_t* topk_ids_out,
+                       const moe_experts_t* shared, void* out, int32_t out_dt, int32_t y_dt, int32_t* topk_ids_out,
                        float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
     moe_status_t st = validate_route(x, x_dt, T, H, w_router, E, k, score);
     if (st) return st;
@@ -257,11 +269,14 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
     const bool ok_combo = (x_dt == MOE_F32 && wdt == MOE_F32) || (x_dt == MOE_BF16 && (wdt == MOE_BF16 || wdt == MOE_E4M3));
     if (!ok_combo) return fail(MOE_ERR_UNSUPPORTED, "layer: x dtype %d with weights %d", x_dt, wdt);
     if (out_dt != MOE_F32 && out_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "layer: out dtype %d", out_dt);
+    if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "layer: y dtype %d", y_dt);
+    if (y_dt == MOE_E4M3 && (wdt != MOE_E4M3 || H % 256))
+        return fail(MOE_ERR_UNSUPPORTED, "layer: E4M3 y needs E4M3 weights and H %% 256 == 0 (H=%d)", H);
     if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "layer: T*k too large");
     if (T == 0) return MOE_OK;
     if (!out || !aligned16(out) || !aligned16(x)) return fail(MOE_ERR_INVALID, "layer: null or misaligned x/out");
     const int has_sh = shared ? 1 : 0;
-    const LayerWs L = layer_ws(T, H, E, k, I, x_dt, wdt, has_sh, out_dt);
+    const LayerWs L = layer_ws(T, H, E, k, I, x_dt, wdt, has_sh, out_dt, y_dt);
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u)) return fail(MOE_ERR_WORKSPACE, "layer: workspace");
     uint8_t* w8 = (uint8_t*)ws;
     hipStream_t s = (hipStream_t)stream;
@@ -289,12 +304,15 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
         p.dt = wdt; p.a = a; p.a_scale = as; p.src = src; p.src_div = k;
         p.offsets = offsets; p.G = E; p.R_max = R; p.routed = to_bank(routed);
         p.a_sh = a; p.a_sh_scale = as; p.S = has_sh ? T : 0; p.has_shared = has_sh; p.shared = to_bank(shared);
-        p.H = H; p.I = I; p.y = w8 + L.yperm; p.y_sh = has_sh ? w8 + L.ysh : nullptr; p.y_bf16 = ybf;
+        p.H = H; p.I = I; p.y = w8 + L.yperm; p.y_sh = has_sh ? w8 + L.ysh : nullptr;
+        p.y_bf16 = y_dt == MOE_BF16; p.y_e4m3 = y_dt == MOE_E4M3; p.y_scale = (float*)(w8 + L.yscale);
+        p.y_sh_bf16 = ybf;
         e = moe::launch_gffn(p, w8 + L.gffn, s);
     }
     if (e == hipSuccess)
-        e = moe::launch_combine(w8 + L.yperm, has_sh ? w8 + L.ysh : nullptr, ybf, dest, tw, T, k, H, out,
-                                out_dt == MOE_BF16, s);
+        e = moe::launch_combine(w8 + L.yperm, y_dt == MOE_E4M3 ? 2 : y_dt == MOE_BF16 ? 1 : 0,
+                                (const float*)(w8 + L.yscale), has_sh ? w8 + L.ysh : nullptr, ybf, dest, tw, T, k, H,
+                                out, out_dt == MOE_BF16, s);
     return hip_check(e, "moe_layer");
 }
 

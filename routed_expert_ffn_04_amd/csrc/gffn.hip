@@ -220,6 +220,7 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     A.offsets = p.offsets; A.G = p.G; A.R_max = p.R_max; A.S = p.has_shared ? p.S : 0;
     A.routed = p.routed; A.shared = p.shared; A.H = p.H; A.I = p.I;
     A.y = p.y; A.y_sh = p.y_sh; A.y_bf16 = p.y_bf16;
+    A.y_e4m3 = p.y_e4m3; A.y_scale = p.y_scale; A.y_sh_bf16 = p.y_sh_bf16;
     const size_t rows = (size_t)p.R_max + A.S;
     const int eb = p.dt == DT_F32 ? 4 : p.dt == DT_BF16 ? 2 : 1;
     const ClassSpec cs = class_spec(p.dt, p.H, p.I, p.R_max, A.S);

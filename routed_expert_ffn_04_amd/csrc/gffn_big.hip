@@ -345,7 +345,40 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
         }
     } else {
         void* yb = gi.shared ? A.y_sh : A.y;
-        if (FP8) {
+        const int ybf = gi.shared ? A.y_sh_bf16 : A.y_bf16;
+        if (FP8 && !gi.shared && A.y_e4m3) {
+            // y as e4m3 per row and 128-column block (the FP8 combine): the
+            // block of a row is split over waves wn and wn^1 (64 columns each)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float mx = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(acc8[i][j][q]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                if (lane < 16) S.red[wn * kBigM + wm * 128 + i * 16 + lane] = mx;
+            }
+            __syncthreads();
+            const int pw = wn & ~1;   // first wave of the pair
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = wm * 128 + i * 16 + lane % 16;
+                const int yr = S.out_row[r];
+                if (yr < 0) continue;
+                const float amax = fmaxf(S.red[pw * kBigM + r], S.red[(pw + 1) * kBigM + r]);
+                // scale amax / 448 (within an ulp); codes y * (448 / amax)
+                const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+                const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
+                if ((wn & 1) == 0 && lane < 16) A.y_scale[(size_t)yr * (H / 128) + (n0 + wn * 64) / 128] = sc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *(uint32_t*)((uint8_t*)yb + (size_t)yr * H + n0 + wn * 64 + 16 * j + 4 * (lane / 16)) =
+                        f32x4_to_e4m3x4(acc8[i][j][0] * inv, acc8[i][j][1] * inv, acc8[i][j][2] * inv,
+                                        acc8[i][j][3] * inv);
+            }
+        } else if (FP8) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = wm * 128 + i * 16 + lane % 16;
@@ -355,7 +388,7 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                 for (int j = 0; j < 4; ++j) {
                     const size_t o = (size_t)yr * H + n0 + wn * 64 + 16 * j + 4 * (lane / 16);
                     const f32x4 v = acc8[i][j];
-                    if (A.y_bf16) {
+                    if (ybf) {
                         const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
                         const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
                         *(uint2*)((uint16_t*)yb + o) = make_uint2(lo, hi);
@@ -375,7 +408,7 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const size_t o = (size_t)yr * H + n0 + wn * 64 + 32 * j + lane % 32;
-                        if (A.y_bf16) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc16[i][j][v]);
+                        if (ybf) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc16[i][j][v]);
                         else ((float*)yb)[o] = acc16[i][j][v];
                     }
                 }

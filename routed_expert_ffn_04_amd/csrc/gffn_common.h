@@ -52,7 +52,9 @@ struct GArgs {
     Bank routed, shared;
     int H, I;
     uint8_t* h; float* h_scale;        // [R_max + S][I], [R_max + S][I/128]
-    void* y; void* y_sh; int y_bf16;
+    void* y; void* y_sh; int y_bf16;   // routed outputs bf16 (else fp32 unless y_e4m3)
+    int y_e4m3; float* y_scale;        // routed outputs as e4m3 + [R_max][H/128] scales (large fp8 tiles)
+    int y_sh_bf16;                     // shared outputs bf16 (else fp32)
 };
 
 struct GroupInfo {

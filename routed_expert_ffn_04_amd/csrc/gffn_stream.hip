@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void stream_down_kernel(GArgs A, TileList L) {
 #pragma unroll
             for (int w = 0; w < KS; ++w) v += red[w][row][col];
             const size_t yr = gi.shared ? (size_t)r : (size_t)(gi.p0 + r);
-            if (A.y_bf16) ((uint16_t*)yb)[yr * H + nt0 + col] = (uint16_t)f32_to_bf16_bits(v);
+            if (gi.shared ? A.y_sh_bf16 : A.y_bf16) ((uint16_t*)yb)[yr * H + nt0 + col] = (uint16_t)f32_to_bf16_bits(v);
             else ((float*)yb)[yr * H + nt0 + col] = v;
         }
     }

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void tile_down_kernel(GArgs A, TileList L) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int c = n0 + wn * 64 + j * 16 + lane % 16;
-                    if (A.y_bf16) ((uint16_t*)yb)[(size_t)yr * H + c] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
+                    if (gi.shared ? A.y_sh_bf16 : A.y_bf16) ((uint16_t*)yb)[(size_t)yr * H + c] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
                     else ((float*)yb)[(size_t)yr * H + c] = acc[i][j][q];
                 }
             }

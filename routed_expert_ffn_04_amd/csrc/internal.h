@@ -24,8 +24,9 @@ hipError_t launch_quant_e4m3(const void* x, int x_bf16, int rows, int cols, uint
                              float* scale, hipStream_t s);
 
 // combine.hip
-hipError_t launch_combine(const void* y_perm, const void* y_sh, int y_bf16, const int32_t* dest,
-                          const float* w, int T, int k, int H, void* out, int out_bf16,
+// y_mode: 0 fp32, 1 bf16, 2 e4m3 codes + y_scale [rows][H/128]
+hipError_t launch_combine(const void* y_perm, int y_mode, const float* y_scale, const void* y_sh, int y_sh_bf16,
+                          const int32_t* dest, const float* w, int T, int k, int H, void* out, int out_bf16,
                           hipStream_t s);
 
 // gffn.hip ------------------------------------------------------------------
@@ -42,7 +43,9 @@ struct GffnProblem {
     const void* a_sh; const float* a_sh_scale; int S; int has_shared;
     Bank shared;
     int H, I;
-    void* y; void* y_sh; int y_bf16;
+    void* y; void* y_sh; int y_bf16;   // routed outputs bf16 (else fp32 unless y_e4m3)
+    int y_e4m3; float* y_scale;        // routed outputs as e4m3 + [R_max][H/128] scales
+    int y_sh_bf16;                     // shared outputs bf16 (else fp32)
 };
 
 size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt);

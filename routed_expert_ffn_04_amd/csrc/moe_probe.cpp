@@ -214,7 +214,8 @@ int main(int argc, char** argv) {
                 CM(moe_grouped_ffn(a, dt, dt == MOE_E4M3 ? as : nullptr, nullptr, 1, d_offs, G, R, &routed.d,
                                    S > 0 ? (const uint8_t*)a + (size_t)R * H * eb : nullptr,
                                    (S > 0 && dt == MOE_E4M3) ? as + (size_t)R * (H / 128) : nullptr, S,
-                                   S > 0 ? &shared.d : nullptr, y, S > 0 ? y_sh : nullptr, MOE_BF16, ws, wsb, st));
+                                   S > 0 ? &shared.d : nullptr, y, MOE_BF16, nullptr, S > 0 ? y_sh : nullptr, MOE_BF16,
+                                   ws, wsb, st));
             };
             run();
             CK(hipEventRecord(e0, st));
@@ -234,7 +235,7 @@ int main(int argc, char** argv) {
     else if (mode == "skew") { T = 4096; w_dt = MOE_BF16; out_dt = MOE_F32; bias = true; }
     else if (mode == "prefill") { T = 16384; w_dt = MOE_E4M3; out_dt = MOE_BF16; }
     else if (mode != "file") { fprintf(stderr, "unknown mode %s\n", mode.c_str()); return 1; }
-    int H = 7168, E = 256, k = 8, I = 2048, score = MOE_SIGMOID, has_shared = 1;
+    int H = 7168, E = 256, k = 8, I = 2048, score = MOE_SIGMOID, has_shared = 1, y_dt = -1;
     void* x = nullptr;
     float* wr = nullptr;
     float* b = nullptr;
@@ -244,6 +245,7 @@ int main(int argc, char** argv) {
         x_dt = dt_of(m["x_dt"]); w_dt = dt_of(m["w_dt"]); out_dt = dt_of(m["out_dt"]);
         score = m["score"] == "softmax" ? MOE_SOFTMAX : MOE_SIGMOID;
         has_shared = std::stoi(m["shared"]);
+        if (m.count("y_dt")) y_dt = dt_of(m["y_dt"]);
         x = load_file(dir + "/x.bin", (size_t)T * H * (x_dt == MOE_F32 ? 4 : 2));
         wr = (float*)load_file(dir + "/w_router.bin", (size_t)H * E * 4);
         if (std::stoi(m["bias"])) b = (float*)load_file(dir + "/bias.bin", (size_t)E * 4);
@@ -262,12 +264,13 @@ int main(int argc, char** argv) {
     BankBuf routed = make_bank(E, H, I, w_dt, 100);
     BankBuf shared = make_bank(1, H, I, w_dt, 200);
     void* out = dalloc((size_t)T * H * (out_dt == MOE_BF16 ? 2 : 4));
-    const size_t wsb = moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt);
+    if (y_dt < 0) y_dt = out_dt;
+    const size_t wsb = moe_layer_workspace_size(T, H, E, k, I, x_dt, w_dt, has_shared, out_dt, y_dt);
     void* ws = dalloc(wsb);
     CK(hipDeviceSynchronize());
 
     auto run = [&]() {
-        CM(moe_layer(x, x_dt, T, H, wr, b, E, k, score, &routed.d, has_shared ? &shared.d : nullptr, out, out_dt, nullptr,
+        CM(moe_layer(x, x_dt, T, H, wr, b, E, k, score, &routed.d, has_shared ? &shared.d : nullptr, out, out_dt, y_dt, nullptr,
                      nullptr, nullptr, ws, wsb, st));
     };
     run();

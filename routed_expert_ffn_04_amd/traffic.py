@@ -75,6 +75,8 @@ def pmc_pass(counter, probe_args, work, tag):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--configs", type=int, nargs="+", default=[2, 5])
+    ap.add_argument("--fp8-combine-configs", type=int, nargs="*", default=[],
+                    help="fp8 layer workloads to measure also with the FP8 combine")
     ap.add_argument("--calls", type=int, default=2, help="timed calls per probe run (one more is the warm-up)")
     ap.add_argument("--work", default="/tmp/moe_traffic", help="scratch (dumped inputs, raw counter files)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
@@ -93,14 +95,16 @@ def main():
         print(f"calibration {counter}: {kib:.0f} KiB per 1 GiB copy -> {gib / kib:.1f} bytes per KiB", flush=True)
 
     result = {"sources_sha256": sources_digest(), "calibration": cal, "workloads": {}}
-    for cid in args.configs:
-        d = os.path.join(args.work, f"inputs_c{cid}")
-        run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(cid), "--dump-inputs", d],
-            os.path.join(args.work, f"dump_c{cid}.log"))
+    runs = [(c, False) for c in args.configs] + [(c, True) for c in args.fp8_combine_configs]
+    for cid, fp8c in runs:
+        tag = f"c{cid}" + ("f" if fp8c else "")
+        d = os.path.join(args.work, f"inputs_{tag}")
+        run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(cid), "--dump-inputs", d]
+            + (["--fp8-combine"] if fp8c else []), os.path.join(args.work, f"dump_{tag}.log"))
         ncalls = args.calls + 1
         rec = {"calls": ncalls, "kernels": {}}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            per = pmc_pass(counter, ["file", d, str(args.calls)], args.work, f"c{cid}")
+            per = pmc_pass(counter, ["file", d, str(args.calls)], args.work, tag)
             tot = 0.0
             for k, vals in per.items():
                 if not any(s in k for s in GFFN_KERNELS):
@@ -111,9 +115,12 @@ def main():
             rec[counter.lower().replace("_size", "_bytes")] = round(tot)
         rec["bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
         rec["command"] = (f"python -m routed_expert_ffn_04_amd.traffic --configs {' '.join(map(str, args.configs))}"
-                          f" (probe: moe_probe file <dump of bench.py --config {cid}> {args.calls})")
-        result["workloads"][NAMES[cid]] = rec
-        print(f"config {cid}: grouped FFN per call: fetch {rec['fetch_bytes'] / 1e9:.3f} GB, "
+                          + (f" --fp8-combine-configs {' '.join(map(str, args.fp8_combine_configs))}"
+                             if args.fp8_combine_configs else "")
+                          + f" (probe: moe_probe file <dump of bench.py --config {cid}"
+                          + (" --fp8-combine" if fp8c else "") + f"> {args.calls})")
+        result["workloads"][NAMES[cid] + ("+fp8-combine" if fp8c else "")] = rec
+        print(f"config {cid}{' fp8 combine' if fp8c else ''}: grouped FFN per call: fetch {rec['fetch_bytes'] / 1e9:.3f} GB, "
               f"write {rec['write_bytes'] / 1e9:.3f} GB", flush=True)
     os.makedirs(os.path.dirname(args.out), exist_ok=True)
     with open(args.out, "w") as f:

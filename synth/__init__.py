@@ -207,6 +207,9 @@ class Workload:
     a_q: Optional[torch.Tensor] = None        # [sum m][H] uint8 (routed groups, then shared)
     a_s: Optional[torch.Tensor] = None        # [sum m][H/128] fp32
     meta: dict = field(default_factory=dict)
+    # routed expert outputs before the combine: None = out_dt precision,
+    # 'e4m3' = per-1x128 fp8 (the FP8 combine)
+    y_dt: Optional[str] = None
 
 
 def _bank(n, H, I, dt, seed, streams, std, device, experts=None) -> Bank:

@@ -38,9 +38,13 @@ def test_workspace_queries_are_host_only():
     L = moe.lib()
     assert L.moe_route_workspace_size(128, 256) >= 128 * 256 * 4
     assert L.moe_permute_workspace_size(16384, 8, 256) > 0
-    a = L.moe_layer_workspace_size(128, 7168, 256, 8, 2048, 1, 1, 1, 0)
-    b = L.moe_layer_workspace_size(16384, 7168, 256, 8, 2048, 1, 2, 1, 1)
+    a = L.moe_layer_workspace_size(128, 7168, 256, 8, 2048, 1, 1, 1, 0, 0)
+    b = L.moe_layer_workspace_size(16384, 7168, 256, 8, 2048, 1, 2, 1, 1, 1)
     assert b > a > 128 * 8 * 7168 * 4
+    # fp8 expert outputs: 1 byte per value plus a scale per 128 columns instead of 2
+    c = L.moe_layer_workspace_size(16384, 7168, 256, 8, 2048, 1, 2, 1, 1, 2)
+    R = 16384 * 8
+    assert b - c >= R * 7168 - R * 56 * 4 - 4096
 
 
 P = 0x1000  # a non-null dummy address; validation fails before any use
@@ -71,9 +75,11 @@ def test_permute_and_combine_validation():
     assert L.moe_permute(P, 4, 2, 2000, P, P, P, P, P, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_permute(P, 4, 2, 8, None, P, P, P, P, 1 << 20, None) == moe.MOE_ERR_INVALID
     assert L.moe_permute(P, 4, 2, 8, P, P, P, P, P, 4, None) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_combine(P, None, 0, P, P, 4, 2, 100, P, 0, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_combine(None, None, 0, P, P, 4, 2, 128, P, 0, None) == moe.MOE_ERR_INVALID
-    assert L.moe_combine(None, None, 0, None, None, 0, 2, 128, None, 0, None) == moe.MOE_OK
+    assert L.moe_combine(P, 0, None, None, 0, P, P, 4, 2, 100, P, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(None, 0, None, None, 0, P, P, 4, 2, 128, P, 0, None) == moe.MOE_ERR_INVALID
+    assert L.moe_combine(None, 0, None, None, 0, None, None, 0, 2, 128, None, 0, None) == moe.MOE_OK
+    assert L.moe_combine(P, 2, None, None, 0, P, P, 4, 2, 128, P, 0, None) == moe.MOE_ERR_INVALID   # e4m3 y, no scales
+    assert L.moe_combine(P, 2, P, P, 2, P, P, 4, 2, 128, P, 0, None) == moe.MOE_ERR_UNSUPPORTED     # e4m3 y_sh
     assert L.moe_quant_e4m3_1x128(P, 1, 4, 100, P, P, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_quant_e4m3_1x128(None, 1, 0, 128, None, None, None) == moe.MOE_OK
 
@@ -86,11 +92,15 @@ def _bank(n, H, I, dt, scales=True):
 def test_grouped_ffn_validation():
     L = moe.lib()
     b = _bank(8, 256, 256, moe.BF16)
-    call = lambda a_dt, bank, y_dt=0, ws=1 << 40, G=8, sh=None, S=0: L.moe_grouped_ffn(
-        P, a_dt, None, P, 2, P, G, 64, ctypes.byref(bank), None, None, S,
-        ctypes.byref(sh) if sh else None, P, None, y_dt, P, ws, None)
+    call = lambda a_dt, bank, y_dt=0, ws=1 << 40, G=8, sh=None, S=0, a_s=None, y_s=None: L.moe_grouped_ffn(
+        P, a_dt, a_s, P, 2, P, G, 64, ctypes.byref(bank), None, None, S,
+        ctypes.byref(sh) if sh else None, P, y_dt, y_s, None, 0, P, ws, None)
     assert call(moe.F32, b) == moe.MOE_ERR_UNSUPPORTED            # activation/weight dtype mismatch
-    assert call(moe.BF16, b, y_dt=2) == moe.MOE_ERR_UNSUPPORTED   # e4m3 output
+    assert call(moe.BF16, b, y_dt=2) == moe.MOE_ERR_UNSUPPORTED   # e4m3 output needs e4m3 weights
+    e8 = _bank(8, 384, 256, moe.E4M3)
+    assert call(moe.E4M3, e8, y_dt=2, a_s=P, y_s=P) == moe.MOE_ERR_UNSUPPORTED   # ... and H % 256 == 0
+    e8 = _bank(8, 512, 256, moe.E4M3)
+    assert call(moe.E4M3, e8, y_dt=2, a_s=P) == moe.MOE_ERR_INVALID              # ... and scales
     assert call(moe.BF16, b, G=7) == moe.MOE_ERR_INVALID          # bank size != G
     assert call(moe.E4M3, _bank(8, 256, 256, moe.E4M3, scales=False)) == moe.MOE_ERR_INVALID
     assert call(moe.BF16, _bank(8, 200, 256, moe.BF16)) == moe.MOE_ERR_UNSUPPORTED
@@ -101,10 +111,11 @@ def test_grouped_ffn_validation():
 def test_layer_validation():
     L = moe.lib()
     b = _bank(8, 256, 256, moe.BF16)
-    f = lambda xdt, bank, E=8, k=2, ws=1 << 40, out_dt=0: L.moe_layer(
-        P, xdt, 16, 256, P, None, E, k, 1, ctypes.byref(bank), None, P, out_dt, None, None, None, P, ws, None)
+    f = lambda xdt, bank, E=8, k=2, ws=1 << 40, out_dt=0, y_dt=0: L.moe_layer(
+        P, xdt, 16, 256, P, None, E, k, 1, ctypes.byref(bank), None, P, out_dt, y_dt, None, None, None, P, ws, None)
     assert f(moe.F32, b) == moe.MOE_ERR_UNSUPPORTED          # f32 x with bf16 weights
     assert f(moe.BF16, b, E=9) == moe.MOE_ERR_INVALID        # bank n != E
     assert f(moe.BF16, b, k=9) == moe.MOE_ERR_INVALID
     assert f(moe.BF16, b, ws=128) == moe.MOE_ERR_WORKSPACE
     assert f(moe.BF16, b, out_dt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert f(moe.BF16, b, y_dt=2) == moe.MOE_ERR_UNSUPPORTED    # fp8 combine needs e4m3 weights

@@ -45,11 +45,13 @@ def _sample(T, n, seed):
     return sorted(set([0, T - 1] + rng.choice(T, size=n, replace=False).tolist()))
 
 
-@pytest.mark.parametrize("cid,nsample", [(1, None), (2, 6), (3, 6), (5, 4)])
-def test_layer_config_full_size(cid, nsample):
-    print(f"config {cid}: generating", flush=True)
+@pytest.mark.parametrize("cid,nsample,fp8c", [(1, None, False), (2, 6, False), (3, 6, False), (5, 4, False),
+                                              (5, 3, True)])
+def test_layer_config_full_size(cid, nsample, fp8c):
+    print(f"config {cid}{' with the fp8 combine' if fp8c else ''}: generating", flush=True)
     wl = synth.config(cid, device=DEV)
-    run = bench.LayerRunner(wl, DEV)
+    wl.y_dt = "e4m3" if fp8c else None
+    run = bench.LayerRunner(wl, DEV, fp8_combine=fp8c)
     for _, f in run.calls():
         f()
     torch.cuda.synchronize()

@@ -162,16 +162,20 @@ GROUPED_CASES = [
 
 
 @pytest.mark.parametrize("gm,sm,H,I,dt", GROUPED_CASES)
-@pytest.mark.parametrize("y_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("y_dt", ["f32", "bf16", "e4m3"])
 def test_grouped_ffn_parity(gm, sm, H, I, dt, y_dt):
+    if y_dt == "e4m3" and (dt != "e4m3" or H % 256):
+        pytest.skip("e4m3 expert outputs: e4m3 weights and H % 256 == 0 only")
     print(f"grouped gm={gm} sm={sm} H={H} I={I} {dt} y={y_dt}", flush=True)
-    wl = synth.make_grouped(gm, sm, H, I, dt=dt, seed=sum(gm) + sm, y_dt=y_dt)
+    fp8_y = y_dt == "e4m3"
+    wl = synth.make_grouped(gm, sm, H, I, dt=dt, seed=sum(gm) + sm, y_dt="bf16" if fp8_y else y_dt)
+    wl.y_dt = "e4m3" if fp8_y else None
     ref = om.grouped_ffn(wl)
     wl = to_dev(wl)
     G = len(gm)
     offs = torch.tensor(np.concatenate([[0], np.cumsum(gm)]), dtype=torch.int32, device=DEV)
     R = int(sum(gm))
-    ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
+    ydt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[y_dt]
     if dt == "e4m3":
         a, a_s = wl.a_q, wl.a_s
         a_sh, a_sh_s = (wl.a_q[R:], wl.a_s[R:]) if sm else (None, None)
@@ -182,7 +186,10 @@ def test_grouped_ffn_parity(gm, sm, H, I, dt, y_dt):
                               a_sh=a_sh, a_sh_scale=a_sh_s,
                               shared=moe.Experts.from_bank(wl.shared) if sm else None, y_dtype=ydt)
     torch.cuda.synchronize()
-    yc = y.float().cpu().numpy()
+    if fp8_y:
+        yc = codecs.dequant_e4m3_1x128(y[0].cpu().numpy(), y[1].cpu().numpy())
+    else:
+        yc = y.float().cpu().numpy()
     starts = np.concatenate([[0], np.cumsum(gm)])
     for g in range(G):
         check_out(yc[starts[g]:starts[g + 1]], ref[g][1], dt == "e4m3", f"group {g}")
@@ -192,20 +199,33 @@ def test_grouped_ffn_parity(gm, sm, H, I, dt, y_dt):
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("y_dt,out_dt,shared", [("f32", "f32", True), ("bf16", "bf16", True), ("f32", "bf16", False)])
+@pytest.mark.parametrize("y_dt,out_dt,shared", [("f32", "f32", True), ("bf16", "bf16", True), ("f32", "bf16", False),
+                                               ("e4m3", "bf16", True), ("e4m3", "f32", False)])
 def test_combine_parity(y_dt, out_dt, shared):
     T, k, H = 50, 4, 384
     rng = np.random.default_rng(1)
     R = T * k
     dest = rng.permutation(R).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
-    ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
-    yp = synth.normal((R, H), 9, 1, 1.0, ydt)
-    ysh = synth.normal((T, H), 9, 2, 1.0, ydt) if shared else None
-    ref = om.combine(yp.float().numpy().astype(np.float64), None if ysh is None else ysh.float().numpy(), dest, w, k)
+    ysc = None
+    if y_dt == "e4m3":
+        # codes of every finite value (no 0x7F / 0xFF) and positive fp32 block scales
+        codes = rng.integers(0, 0x7F, size=(R, H), dtype=np.uint8) | (rng.integers(0, 2, size=(R, H)) << 7).astype(np.uint8)
+        scales = np.exp(rng.uniform(-6, 2, size=(R, H // 128))).astype(np.float32)
+        yp = torch.from_numpy(codes)
+        ysc = torch.from_numpy(scales)
+        yref = codecs.dequant_e4m3_1x128(codes, scales)
+        ysh = synth.normal((T, H), 9, 2, 1.0, torch.bfloat16) if shared else None
+    else:
+        ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
+        yp = synth.normal((R, H), 9, 1, 1.0, ydt)
+        yref = yp.float().numpy().astype(np.float64)
+        ysh = synth.normal((T, H), 9, 2, 1.0, ydt) if shared else None
+    ref = om.combine(yref, None if ysh is None else ysh.float().numpy(), dest, w, k)
     ref = om.round_to(ref, out_dt)
     out = moe.combine(yp.to(DEV), None if ysh is None else ysh.to(DEV), torch.from_numpy(dest).to(DEV),
-                      torch.from_numpy(w).to(DEV), out_dtype=torch.float32 if out_dt == "f32" else torch.bfloat16)
+                      torch.from_numpy(w).to(DEV), out_dtype=torch.float32 if out_dt == "f32" else torch.bfloat16,
+                      y_scale=None if ysc is None else ysc.to(DEV))
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     # fp32 accumulation vs the oracle's fp64: a few ulps (then the output rounding)
@@ -220,20 +240,25 @@ LAYER_CASES = [
     dict(T=100, H=512, E=32, k=4, I=256, x_dt="bf16", w_dt="bf16", out_dt="f32", score="sigmoid", shared=True),
     dict(T=77, H=512, E=16, k=3, I=384, x_dt="bf16", w_dt="e4m3", out_dt="bf16", score="sigmoid", shared=True),
     dict(T=200, H=256, E=64, k=8, I=256, x_dt="bf16", w_dt="bf16", out_dt="bf16", score="softmax", shared=False),
+    # the FP8 combine: routed outputs as e4m3 per 1x128 before the weighted reduce
+    dict(T=90, H=512, E=16, k=4, I=256, x_dt="bf16", w_dt="e4m3", out_dt="bf16", score="sigmoid", shared=True,
+         y_dt="e4m3"),
 ]
 
 
-@pytest.mark.parametrize("cfg", LAYER_CASES, ids=lambda c: f"{c['w_dt']}-T{c['T']}-E{c['E']}")
+@pytest.mark.parametrize("cfg", LAYER_CASES, ids=lambda c: f"{c['w_dt']}-T{c['T']}-E{c['E']}-y{c.get('y_dt')}")
 def test_layer_parity(cfg):
     print(f"layer {cfg}", flush=True)
     c = dict(cfg)
+    y_dt = c.pop("y_dt", None)
     wl = synth.make_layer(c.pop("T"), c.pop("H"), c.pop("E"), c.pop("k"), c.pop("I"), seed=123, **c)
+    wl.y_dt = y_dt
     ref = om.moe_layer(wl)
     wl = to_dev(wl)
     out, ids, w, counts = moe.layer(wl.x, wl.w_router, wl.bias, wl.k, wl.score, moe.Experts.from_bank(wl.routed),
                                     moe.Experts.from_bank(wl.shared) if wl.shared is not None else None,
                                     out_dtype=torch.float32 if wl.out_dt == "f32" else torch.bfloat16,
-                                    want_routing=True)
+                                    want_routing=True, y_dtype=torch.uint8 if y_dt == "e4m3" else None)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
