@@ -18,6 +18,8 @@ Floating point: fp64 everywhere except where the method fixes a precision:
   * router logits are fp32 fused-multiply-add chains (router_chain.c), because
     the top-k decision must be taken in the same precision as the GPU's;
   * fp8 quantisation (activations and h) is fp32 arithmetic with fp32 scales;
+    MX quantisation (MXFP8 activations and h of MXFP4 layers, mx.py) is exact
+    from the fp32 value (power-of-two scales);
   * h is rounded to bf16 for bf16 layers, and outputs to their storage type.
 Every reading of a point the pages leave open is listed in the design notes.
 """
@@ -28,7 +30,7 @@ import os
 
 import numpy as np
 
-from . import codecs
+from . import codecs, mx
 from .build import LIB as _ROUTER_LIB, build as _build_router
 
 _lib = None
@@ -147,6 +149,9 @@ def bank_expert_f64(bank, e: int):
     if bank.dt in ("f32", "bf16"):
         f = lambda t: t[e].float().cpu().numpy().astype(np.float64)
         return f(bank.w_gate), f(bank.w_up), f(bank.w_down)
+    if bank.dt == "mxfp4":
+        f = lambda w, s: mx.mxfp4_matrix(w[e].cpu().numpy(), s[e].cpu().numpy())
+        return f(bank.w_gate, bank.s_gate), f(bank.w_up, bank.s_up), f(bank.w_down, bank.s_down)
     assert bank.dt == "e4m3"
 
     def dq(q, s):
@@ -168,7 +173,9 @@ def expert_ffn(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_
       'f32'  : unrounded;
       'bf16' : rounded to bf16 (nearest even);
       'e4m3' : fl32(h), then quantised per row and 128-column block exactly as
-               the activations are (quant_e4m3_1x128) and dequantised.
+               the activations are (quant_e4m3_1x128) and dequantised;
+      'mxfp8': fl32(h), then MXFP8 per row and 32-column block (mx.py), as
+               the activations of an MXFP4 layer are.
     """
     g = a @ wg.T
     u = a @ wu.T
@@ -178,6 +185,8 @@ def expert_ffn(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_
     elif h_mode == "e4m3":
         q, s = codecs.quant_e4m3_1x128(h.astype(np.float32))
         h = codecs.dequant_e4m3_1x128(q, s)
+    elif h_mode == "mxfp8":
+        h = mx.mxfp8_round_trip(h.astype(np.float32))
     elif h_mode != "f32":
         raise ValueError(h_mode)
     y = h @ wd.T
@@ -205,7 +214,7 @@ def round_y(v: np.ndarray, y_dt: str) -> np.ndarray:
 
 
 def h_mode_for(w_dt: str) -> str:
-    return {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3"}[w_dt]
+    return {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "mxfp4": "mxfp8"}[w_dt]
 
 
 # ---------------------------------------------------------- combine [P2] "combine reduce"
@@ -234,11 +243,14 @@ def layer_inputs(wl):
 
 def activation_rows(wl, x32: np.ndarray) -> np.ndarray:
     """The rows the experts consume, fp64: the input itself for f32/bf16
-    layers; for e4m3 layers the per-1x128 quantised-and-dequantised input
-    (the quantisation is done once per token and shared by its k copies)."""
+    layers; for e4m3 layers the per-1x128 quantised-and-dequantised input,
+    for MXFP4 layers the MXFP8 (per-32) one (the quantisation is done once
+    per token and shared by its k copies)."""
     if wl.w_dt == "e4m3":
         q, s = codecs.quant_e4m3_1x128(x32)
         return codecs.dequant_e4m3_1x128(q, s)
+    if wl.w_dt == "mxfp4":
+        return mx.mxfp8_round_trip(x32)
     return x32.astype(np.float64)
 
 
@@ -321,6 +333,12 @@ def grouped_ffn(wl, group_sample=None) -> dict:
 
         def rows_of(idx):
             return (_E4M3_TABLE[qa[idx]].reshape(len(idx), H // 128, 128) * sa[idx][:, :, None]).reshape(len(idx), H)
+    elif wl.w_dt == "mxfp4":
+        # rows arrive as bf16 and are consumed as MXFP8 (quantised per 32 columns)
+        xa = wl.x.float().cpu().numpy()
+
+        def rows_of(idx):
+            return mx.mxfp8_round_trip(xa[idx])
     else:
         xa = wl.x.float().cpu().numpy()
 

@@ -161,7 +161,11 @@ class Bank:
     """A bank of n experts; weights stored output-major (K contiguous):
     w_gate, w_up [n][I][H] (element (h, i) of W_gate at [e][i][h]);
     w_down [n][H][I].  dt is 'f32', 'bf16' or 'e4m3' (uint8 codes);
-    e4m3 banks carry scales s_gate, s_up [n][I/128][H/128], s_down [n][H/128][I/128]."""
+    e4m3 banks carry scales s_gate, s_up [n][I/128][H/128], s_down [n][H/128][I/128].
+    'mxfp4' banks hold two E2M1 codes per byte along the reduction index
+    (w_gate, w_up [n][I][H/2], w_down [n][H][I/2], lower index in the low
+    nibble) and one E8M0 scale byte per 32 (s_gate, s_up [n][I][H/32],
+    s_down [n][H][I/32])."""
     n: int
     H: int
     I: int
@@ -212,10 +216,53 @@ class Workload:
     y_dt: Optional[str] = None
 
 
+def _mx_codes_(out: torch.Tensor, seed: int, stream: int, start: int, chunk: int = 1 << 24):
+    """Fill a uint8 tensor with uniform bytes (the low byte of each draw)."""
+    flat = out.view(-1)
+    for c0 in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - c0)
+        flat[c0:c0 + n] = (uniform64(seed, stream, start + c0, n, out.device) & 255).to(torch.uint8)
+    return out
+
+
+def _mx_scales_(out: torch.Tensor, seed: int, stream: int, start: int, e_lo: int, chunk: int = 1 << 24):
+    """Fill a uint8 tensor with E8M0 exponents drawn uniformly from {e_lo, e_lo + 1}."""
+    flat = out.view(-1)
+    for c0 in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - c0)
+        flat[c0:c0 + n] = (e_lo + (_srl(uniform64(seed, stream, start + c0, n, out.device), 40) & 1)).to(torch.uint8)
+    return out
+
+
+# E8M0 exponents of the synthetic MXFP4 banks: scales 2^-8 and 2^-7 with codes
+# uniform over all 16 E2M1 values (mean square 8.5625) give weights of rms
+# about 0.018, the scale of the N(0, 0.02^2) banks of the other dtypes.
+MX_E_LO = 119
+ST_MX_SCALE = 100                     # scale streams: code stream + 100
+
+
+def _bank_mxfp4(idx, H, I, seed, streams, device) -> Bank:
+    """Random MXFP4 experts: uniform E2M1 codes and E8M0 scales drawn
+    directly (no quantisation of real-valued weights)."""
+    sg, su, sd = streams
+    per_w, per_s = H * I // 2, H * I // 32
+    w = [torch.empty((len(idx), I, H // 2), dtype=torch.uint8, device=device) for _ in range(2)]
+    w.append(torch.empty((len(idx), H, I // 2), dtype=torch.uint8, device=device))
+    sc = [torch.empty((len(idx), I, H // 32), dtype=torch.uint8, device=device) for _ in range(2)]
+    sc.append(torch.empty((len(idx), H, I // 32), dtype=torch.uint8, device=device))
+    for j, e in enumerate(idx):
+        for t, st in enumerate((sg, su, sd)):
+            _mx_codes_(w[t][j], seed, st, e * per_w)
+            _mx_scales_(sc[t][j], seed, st + ST_MX_SCALE, e * per_s, MX_E_LO)
+    return Bank(len(idx), H, I, "mxfp4", w[0], w[1], w[2], sc[0], sc[1], sc[2])
+
+
 def _bank(n, H, I, dt, seed, streams, std, device, experts=None) -> Bank:
     """Draw a bank of n experts.  `experts` optionally selects a subset of
     expert indices of the full counter space (regeneration of a slice)."""
     idx = list(range(n)) if experts is None else list(experts)
+    if dt == "mxfp4":
+        return _bank_mxfp4(idx, H, I, seed, streams, device)
     sg, su, sd = streams
     per = H * I
     tgt = torch.float32 if dt in ("f32", "e4m3") else torch.bfloat16
@@ -310,6 +357,8 @@ def make_grouped(group_m, shared_m, H, I, *, dt="e4m3", seed=4, device="cpu", w_
         del xa
     else:
         wl.x = normal((rows, H), seed, ST_X, 1.0, torch.float32 if dt == "f32" else torch.bfloat16, device)
+    if dt == "mxfp4":
+        wl.x_dt = "bf16"
     return wl
 
 
