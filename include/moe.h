@@ -43,7 +43,18 @@
  *    E4M3 banks carry one fp32 scale per 128 x 128 block, in the same order:
  *        s_gate, s_up : [n][I/128][H/128],  s_down : [n][H/128][I/128]
  *    and the represented weight is e4m3_value(code) * scale.
- *  - E4M3 means OCP FP8 E4M3FN (bias 7, max 448, no infinities).
+ *    MXFP4 banks (OCP Microscaling FP4: E2M1 elements, one E8M0 exponent per
+ *    32 consecutive reduction elements) pack two codes per byte along the
+ *    reduction index, the lower index in the low nibble, and carry one
+ *    exponent byte per 32 elements, in the same order:
+ *        w_gate, w_up : [n][I][H/2] bytes,  s_gate, s_up : [n][I][H/32] bytes
+ *        w_down       : [n][H][I/2] bytes,  s_down       : [n][H][I/32] bytes
+ *    The represented weight is e2m1_value(code) * 2^(E - 127).
+ *  - E4M3 means OCP FP8 E4M3FN (bias 7, max 448, no infinities).  MXFP8
+ *    activations are E4M3 codes [rows][cols] with one E8M0 byte per row and
+ *    32 columns [rows][cols/32] (OCP Microscaling), produced by
+ *    moe_quant_mxfp8; E2M1 is 1 sign, 2 exponent (bias 1), 1 mantissa bit:
+ *    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -63,22 +74,23 @@ typedef enum {
     MOE_ERR_HIP = 4
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2, MOE_MXFP4 = 3, MOE_MXFP8 = 4 } moe_dtype_t;
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
 
 /* A bank of n experts (the shared expert is a bank with n = 1).  dt is the
- * weight type: MOE_F32, MOE_BF16, or MOE_E4M3 (then the s_* scales are
- * required).  H and I must be multiples of 128 for every dtype. */
+ * weight type: MOE_F32, MOE_BF16, MOE_E4M3 (fp32 block scales s_* required)
+ * or MOE_MXFP4 (E8M0 exponent bytes s_* required).  H and I are the logical
+ * sizes (elements) and must be multiples of 128 for every dtype. */
 typedef struct {
     int32_t n, H, I;
     int32_t dt;                 /* moe_dtype_t */
-    const void* w_gate;         /* [n][I][H] */
-    const void* w_up;           /* [n][I][H] */
-    const void* w_down;         /* [n][H][I] */
-    const float* s_gate;        /* E4M3 only: [n][I/128][H/128] */
-    const float* s_up;          /* E4M3 only: [n][I/128][H/128] */
-    const float* s_down;        /* E4M3 only: [n][H/128][I/128] */
+    const void* w_gate;         /* [n][I][H]   (MXFP4: [n][I][H/2] bytes) */
+    const void* w_up;           /* [n][I][H]   (MXFP4: [n][I][H/2] bytes) */
+    const void* w_down;         /* [n][H][I]   (MXFP4: [n][H][I/2] bytes) */
+    const void* s_gate;         /* E4M3: fp32 [n][I/128][H/128]; MXFP4: uint8 [n][I][H/32] */
+    const void* s_up;           /* E4M3: fp32 [n][I/128][H/128]; MXFP4: uint8 [n][I][H/32] */
+    const void* s_down;         /* E4M3: fp32 [n][H/128][I/128]; MXFP4: uint8 [n][H][I/32] */
 } moe_experts_t;
 
 /* ---- routing ------------------------------------------------------------
@@ -122,6 +134,17 @@ size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
 moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int32_t cols,
                                   uint8_t* q, float* scale, void* stream);
 
+/* ---- MXFP8 activation quantisation (OCP Microscaling; the activation
+ * format of the MXFP4 expert GEMMs, the FP4 MoE of the pages' Blackwell
+ * deployment: "How DeepSeek inference works", deployment lever table) -------
+ * Per row and block of 32 columns: E = clamp(floor(log2(amax)) - 8 + 127,
+ * 0, 254) (E = 0 for an all-zero block), then q = e4m3(v * 2^(127 - E)) with
+ * the product exact, rounding to nearest even and saturating at 448.
+ * x: [rows][cols] MOE_F32 or MOE_BF16, cols % 32 == 0.
+ * Outputs: q [rows][cols] uint8 E4M3 codes, e8m0 [rows][cols/32] uint8. */
+moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t cols,
+                             uint8_t* q, uint8_t* e8m0, void* stream);
+
 /* ---- grouped FFN --------------------------------------------------------
  * For every routed group g (expert g of `routed`) and permuted row p in
  * [offsets[g], offsets[g+1]):
@@ -132,9 +155,11 @@ moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int
  * rows of a_sh into y_sh.  h' is h at the precision the down projection
  * consumes: F32 weights -> fp32; BF16 -> rounded to bf16 (nearest even);
  * E4M3 -> quantised per row and 128-column block exactly as in
- * moe_quant_e4m3_1x128.  Accumulation is fp32.
- * Supported (a_dt, weight dt): (F32, F32), (BF16, BF16), (E4M3, E4M3);
- * E4M3 activations carry a_scale [rows of a][H/128] (a_sh_scale likewise).
+ * moe_quant_e4m3_1x128; MXFP4 -> MXFP8 per row and 32 columns exactly as in
+ * moe_quant_mxfp8.  Accumulation is fp32.
+ * Supported (a_dt, weight dt): (F32, F32), (BF16, BF16), (E4M3, E4M3),
+ * (MXFP8, MXFP4).  E4M3 activations carry fp32 a_scale [rows of a][H/128],
+ * MXFP8 activations uint8 a_scale [rows of a][H/32] (a_sh_scale likewise).
  * offsets: [G+1] int32 device array with offsets[0] = 0 and
  * offsets[G] <= R_max (R_max, a host value, bounds the routed rows and sizes
  * the launch).  y: [R_max][H] of type y_dt: F32, BF16, or E4M3 = codes
@@ -143,11 +168,11 @@ moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int
  * (E4M3 y needs E4M3 weights and H a multiple of 256; y_scale is ignored
  * otherwise).  y_sh: [S][H] of type y_sh_dt (F32 or BF16).
  * routed->n must equal G; H, I multiples of 128. */
-moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale,
+moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale,
                              const int32_t* src, int32_t src_div,
                              const int32_t* offsets, int32_t G, int32_t R_max,
                              const moe_experts_t* routed,
-                             const void* a_sh, const float* a_sh_scale, int32_t S,
+                             const void* a_sh, const void* a_sh_scale, int32_t S,
                              const moe_experts_t* shared,
                              void* y, int32_t y_dt, float* y_scale, void* y_sh, int32_t y_sh_dt,
                              void* ws, size_t ws_bytes, void* stream);
@@ -167,10 +192,10 @@ moe_status_t moe_combine(const void* y_perm, int32_t y_dt, const float* y_scale,
                          int32_t H, void* out, int32_t out_dt, void* stream);
 
 /* ---- the whole layer ----------------------------------------------------
- * route -> (E4M3 weights: quantise x once per token) -> permute -> grouped
- * FFN over the routed groups and the shared expert -> combine, all enqueued
- * on `stream`.  Supported: x F32 with F32 weights; x BF16 with BF16 or E4M3
- * weights.  y_sh is kept in fp32 when out_dt is F32 and in bf16 when out_dt
+ * route -> (E4M3 or MXFP4 weights: quantise x once per token, per 1x128
+ * block or to MXFP8) -> permute -> grouped FFN over the routed groups and
+ * the shared expert -> combine, all enqueued on `stream`.  Supported: x F32
+ * with F32 weights; x BF16 with BF16, E4M3 or MXFP4 weights.  y_sh is kept in fp32 when out_dt is F32 and in bf16 when out_dt
  * is BF16; the routed expert outputs y_perm in y_dt: F32 or BF16, or E4M3
  * (the FP8 combine; E4M3 weights and H a multiple of 256 only).
  * topk_ids_out [T][k], topk_w_out [T][k], counts_out [E] are optional copies

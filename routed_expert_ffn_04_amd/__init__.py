@@ -6,7 +6,7 @@ kernels behind the C ABI declared in include/moe.h.  The library is loaded on
 first use and a missing library is an error (there is no fallback path).
 
 Entry points mirror the C ABI: route, permute, quant_e4m3_1x128,
-grouped_ffn, combine, layer (plus workspace-size queries).
+quant_mxfp8, grouped_ffn, combine, layer (plus workspace-size queries).
 """
 from __future__ import annotations
 
@@ -19,15 +19,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP4, MXFP8 = 0, 1, 2, 3, 4
 SOFTMAX, SIGMOID = 0, 1
 
-DT = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
+DT = {"f32": F32, "bf16": BF16, "e4m3": E4M3, "mxfp4": MXFP4, "mxfp8": MXFP8}
 SCORE = {"softmax": SOFTMAX, "sigmoid": SIGMOID}
 
 EXPORTS = [
     "moe_route", "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
-    "moe_quant_e4m3_1x128", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
+    "moe_quant_e4m3_1x128", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
     "moe_combine", "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error",
 ]
 
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
             "moe_permute_workspace_size": ([_I32, _I32, _I32], _SZ),
             "moe_quant_e4m3_1x128": ([_P, _I32, _I32, _I32, _P, _P, _P], _I32),
+            "moe_quant_mxfp8": ([_P, _I32, _I32, _I32, _P, _P, _P], _I32),
             "moe_grouped_ffn": ([_P, _I32, _P, _P, _I32, _P, _I32, _I32, ctypes.POINTER(ExpertsT),
                                  _P, _P, _I32, ctypes.POINTER(ExpertsT), _P, _I32, _P, _P, _I32, _P, _SZ, _P], _I32),
             "moe_grouped_ffn_workspace_size": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -118,17 +119,22 @@ def _workspace(nbytes: int, device):
 
 @dataclass
 class Experts:
-    """Device tensors of an expert bank (output-major weights; see moe.h)."""
+    """Device tensors of an expert bank (output-major weights; see moe.h).
+    dt: the weight type (default: from the tensor dtype; MXFP4 banks, packed
+    uint8 [n][I][H/2] with uint8 E8M0 scales, must say MXFP4)."""
     w_gate: object
     w_up: object
     w_down: object
     s_gate: object = None
     s_up: object = None
     s_down: object = None
+    dt: Optional[int] = None
 
     def struct(self) -> ExpertsT:
         n, I, H = self.w_gate.shape
-        dt = _dt_of(self.w_gate)
+        dt = _dt_of(self.w_gate) if self.dt is None else self.dt
+        if dt == MXFP4:
+            H *= 2
         for t in (self.w_gate, self.w_up, self.w_down):
             assert t.is_contiguous() and t.is_cuda
         return ExpertsT(n, H, I, dt, _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down),
@@ -136,7 +142,8 @@ class Experts:
 
     @staticmethod
     def from_bank(bank) -> "Experts":
-        return Experts(bank.w_gate, bank.w_up, bank.w_down, bank.s_gate, bank.s_up, bank.s_down)
+        return Experts(bank.w_gate, bank.w_up, bank.w_down, bank.s_gate, bank.s_up, bank.s_down,
+                       MXFP4 if bank.dt == "mxfp4" else None)
 
 
 # ---------------------------------------------------------------- entry points
@@ -190,6 +197,27 @@ def quant_e4m3_1x128(x, stream=None, out=None):
     return q, s
 
 
+def quant_mxfp8(x, stream=None, out=None):
+    """MXFP8: E4M3 codes [rows][cols] uint8, E8M0 exponents [rows][cols/32] uint8."""
+    import torch
+    rows, cols = x.shape
+    if out is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        e = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, e = out
+    _check(lib().moe_quant_mxfp8(_ptr(x), _dt_of(x), rows, cols, _ptr(q), _ptr(e), _stream(stream)))
+    return q, e
+
+
+def _act_dt(a, a_scale) -> int:
+    """E4M3 codes with fp32 1x128 scales, or MXFP8 codes with uint8 E8M0 exponents."""
+    import torch
+    if a_scale is not None and a_scale.dtype == torch.uint8:
+        return MXFP8
+    return _dt_of(a)
+
+
 def _is_fp8(dtype) -> bool:
     import torch
     return dtype in (torch.uint8, torch.float8_e4m3fn)
@@ -218,7 +246,7 @@ def grouped_ffn(a, offsets, routed: Experts, *, a_scale=None, src=None, src_div:
         y_sh = torch.empty((S, H), dtype=y_sh_dtype, device=dev)
     need = lib().moe_grouped_ffn_workspace_size(R_max, G, S if shared is not None else 0, H, rs.I, rs.dt)
     ws = ws if ws is not None else _workspace(need, dev)
-    _check(lib().moe_grouped_ffn(_ptr(a), _dt_of(a), _ptr(a_scale), _ptr(src), src_div, _ptr(offsets), G, R_max,
+    _check(lib().moe_grouped_ffn(_ptr(a), _act_dt(a, a_scale), _ptr(a_scale), _ptr(src), src_div, _ptr(offsets), G, R_max,
                                  ctypes.byref(rs), _ptr(a_sh), _ptr(a_sh_scale), S,
                                  ctypes.byref(ss) if ss is not None else None,
                                  _ptr(y), _dt_of(y), _ptr(y_scale) if fp8_y else None, _ptr(y_sh),

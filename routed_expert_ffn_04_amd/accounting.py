@@ -26,11 +26,27 @@ def ffn_flops(rows: int, H: int, I: int) -> int:
 
 
 def weight_bytes_per_expert(H: int, I: int, w_dt: str) -> int:
+    if w_dt == "mxfp4":
+        return 3 * H * I // 2 + 3 * H * I // 32      # E2M1 nibbles + one E8M0 byte per 32
     eb = {"f32": 4, "bf16": 2, "e4m3": 1}[w_dt]
     b = 3 * H * I * eb
     if w_dt == "e4m3":
         b += 3 * (H // 128) * (I // 128) * 4
     return b
+
+
+# the type h is stored in between the two projections, by weight type
+H_DT = {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "mxfp4": "mxfp8"}
+
+
+def row_bytes(n: int, dt: str) -> int:
+    """Bytes of one row of n values: e4m3 rows carry an fp32 scale per 128,
+    mxfp8 rows an E8M0 byte per 32."""
+    if dt == "e4m3":
+        return n + n // 128 * 4
+    if dt == "mxfp8":
+        return n + n // 32
+    return n * {"f32": 4, "bf16": 2}[dt]
 
 
 def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w_dt: str, y_dt: str,
@@ -39,14 +55,12 @@ def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w
     routed group (experts with 0 rows are not read).  y_dt: routed outputs
     (e4m3 carries a fp32 scale per 128 values); y_sh_dt: shared outputs
     (default y_dt)."""
-    eb = {"f32": 4, "bf16": 2, "e4m3": 1}
     y_sh_dt = y_sh_dt or y_dt
     touched = sum(1 for m in group_rows if m > 0) + (1 if shared_rows > 0 else 0)
     rows = sum(group_rows) + shared_rows
     b = touched * weight_bytes_per_expert(H, I, w_dt)
-    row = lambda n, dt: n * eb[dt] + (n // 128 * 4 if dt == "e4m3" else 0)
-    b += rows * (row(H, a_dt) + 2 * row(I, w_dt))
-    b += sum(group_rows) * row(H, y_dt) + shared_rows * row(H, y_sh_dt)
+    b += rows * (row_bytes(H, a_dt) + 2 * row_bytes(I, H_DT[w_dt]))
+    b += sum(group_rows) * row_bytes(H, y_dt) + shared_rows * row_bytes(H, y_sh_dt)
     return b
 
 

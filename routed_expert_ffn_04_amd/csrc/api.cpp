@@ -37,13 +37,15 @@ moe_status_t check_bank(const moe_experts_t* b, int n, int H, int I, const char*
     if (!b) return fail(MOE_ERR_INVALID, "%s: null bank", name);
     if (b->n != n) return fail(MOE_ERR_INVALID, "%s: n = %d, expected %d", name, b->n, n);
     if (b->H != H || b->I != I) return fail(MOE_ERR_INVALID, "%s: H/I = %d/%d, expected %d/%d", name, b->H, b->I, H, I);
-    if (b->dt != MOE_F32 && b->dt != MOE_BF16 && b->dt != MOE_E4M3)
+    if (b->dt != MOE_F32 && b->dt != MOE_BF16 && b->dt != MOE_E4M3 && b->dt != MOE_MXFP4)
         return fail(MOE_ERR_UNSUPPORTED, "%s: weight dtype %d", name, b->dt);
     if (!b->w_gate || !b->w_up || !b->w_down) return fail(MOE_ERR_INVALID, "%s: null weight pointer", name);
     if (!aligned16(b->w_gate) || !aligned16(b->w_up) || !aligned16(b->w_down))
         return fail(MOE_ERR_INVALID, "%s: weights must be 16-byte aligned", name);
-    if (b->dt == MOE_E4M3 && (!b->s_gate || !b->s_up || !b->s_down))
-        return fail(MOE_ERR_INVALID, "%s: E4M3 bank without scales", name);
+    if ((b->dt == MOE_E4M3 || b->dt == MOE_MXFP4) && (!b->s_gate || !b->s_up || !b->s_down))
+        return fail(MOE_ERR_INVALID, "%s: E4M3 / MXFP4 bank without scales", name);
+    if (b->dt == MOE_MXFP4 && (((uintptr_t)b->s_gate | (uintptr_t)b->s_up | (uintptr_t)b->s_down) & 3u))
+        return fail(MOE_ERR_INVALID, "%s: MXFP4 exponents must be 4-byte aligned", name);
     return MOE_OK;
 }
 
@@ -51,7 +53,8 @@ moe::Bank to_bank(const moe_experts_t* b) {
     moe::Bank k{};
     if (!b) return k;
     k.wg = b->w_gate; k.wu = b->w_up; k.wd = b->w_down;
-    k.sg = b->s_gate; k.su = b->s_up; k.sd = b->s_down;
+    // fp32 block scales (E4M3) or E8M0 exponent bytes (MXFP4), by the bank's dtype
+    k.sg = (const float*)b->s_gate; k.su = (const float*)b->s_up; k.sd = (const float*)b->s_down;
     return k;
 }
 
@@ -137,15 +140,27 @@ moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int
                      "moe_quant_e4m3_1x128");
 }
 
+moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t cols, uint8_t* q, uint8_t* e8m0,
+                             void* stream) {
+    if (rows < 0 || cols <= 0) return fail(MOE_ERR_INVALID, "quant_mxfp8: rows=%d cols=%d", rows, cols);
+    if (cols % 32) return fail(MOE_ERR_UNSUPPORTED, "quant_mxfp8: cols=%d not a multiple of 32", cols);
+    if (x_dt != MOE_F32 && x_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "quant_mxfp8: x dtype %d", x_dt);
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !e8m0) return fail(MOE_ERR_INVALID, "quant_mxfp8: null pointer");
+    if (!aligned16(x) || ((uintptr_t)q & 7u)) return fail(MOE_ERR_INVALID, "quant_mxfp8: misaligned x or q");
+    return hip_check(moe::launch_quant_mxfp8(x, x_dt == MOE_BF16, rows, cols, q, e8m0, (hipStream_t)stream),
+                     "moe_quant_mxfp8");
+}
+
 // ------------------------------------------------------------------ grouped FFN
 size_t moe_grouped_ffn_workspace_size(int32_t R_max, int32_t G, int32_t S, int32_t H, int32_t I, int32_t w_dt) {
     if (R_max < 0 || G < 0 || S < 0 || H <= 0 || I <= 0) return 0;
     return al(moe::gffn_ws_bytes(R_max, G, S, H, I, w_dt));
 }
 
-moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, const int32_t* src,
+moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale, const int32_t* src,
                              int32_t src_div, const int32_t* offsets, int32_t G, int32_t R_max,
-                             const moe_experts_t* routed, const void* a_sh, const float* a_sh_scale,
+                             const moe_experts_t* routed, const void* a_sh, const void* a_sh_scale,
                              int32_t S, const moe_experts_t* shared, void* y, int32_t y_dt, float* y_scale,
                              void* y_sh, int32_t y_sh_dt, void* ws, size_t ws_bytes, void* stream) {
     if (G < 0 || R_max < 0 || S < 0) return fail(MOE_ERR_INVALID, "grouped_ffn: G=%d R_max=%d S=%d", G, R_max, S);
@@ -161,7 +176,9 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, 
     if (shared && (st = check_bank(shared, 1, H, I, "shared"))) return st;
     const int wdt = ref->dt;
     if (shared && shared->dt != wdt) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: shared/routed dtype differ");
-    if (a_dt != wdt) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: activation dtype %d with weights %d", a_dt, wdt);
+    const int want_adt = wdt == MOE_MXFP4 ? MOE_MXFP8 : wdt;
+    if (a_dt != want_adt)
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: activation dtype %d with weights %d", a_dt, wdt);
     if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3)
         return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y dtype %d", y_dt);
     if (y_dt == MOE_E4M3 && (wdt != MOE_E4M3 || H % 256))
@@ -172,8 +189,10 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, 
     if (R_max > 0 && G > 0 && (!a || !offsets || !y)) return fail(MOE_ERR_INVALID, "grouped_ffn: null a/offsets/y");
     if (R_max > 0 && G > 0 && y_dt == MOE_E4M3 && !y_scale) return fail(MOE_ERR_INVALID, "grouped_ffn: E4M3 y without y_scale");
     if (has_sh && (!a_sh || !y_sh)) return fail(MOE_ERR_INVALID, "grouped_ffn: null a_sh/y_sh");
-    if (wdt == MOE_E4M3 && ((R_max > 0 && G > 0 && !a_scale) || (has_sh && !a_sh_scale)))
-        return fail(MOE_ERR_INVALID, "grouped_ffn: E4M3 activations without scales");
+    if ((wdt == MOE_E4M3 || wdt == MOE_MXFP4) && ((R_max > 0 && G > 0 && !a_scale) || (has_sh && !a_sh_scale)))
+        return fail(MOE_ERR_INVALID, "grouped_ffn: E4M3 / MXFP8 activations without scales");
+    if (wdt == MOE_MXFP4 && (((uintptr_t)a_scale | (uintptr_t)a_sh_scale) & 3u))
+        return fail(MOE_ERR_INVALID, "grouped_ffn: MXFP8 exponents must be 4-byte aligned");
     if ((a && !aligned16(a)) || (a_sh && !aligned16(a_sh))) return fail(MOE_ERR_INVALID, "grouped_ffn: misaligned a");
     if ((R_max == 0 || G == 0) && !has_sh) return MOE_OK;
     if (!ws || ws_bytes < moe_grouped_ffn_workspace_size(R_max, G, has_sh ? S : 0, H, I, wdt))
@@ -183,10 +202,10 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const float* a_scale, 
         return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: G = 0 is not supported");
     }
     moe::GffnProblem p{};
-    p.dt = wdt; p.a = a; p.a_scale = a_scale; p.src = src; p.src_div = src ? src_div : 1;
+    p.dt = wdt; p.a = a; p.a_scale = (const float*)a_scale; p.src = src; p.src_div = src ? src_div : 1;
     p.offsets = offsets; p.G = G; p.R_max = R_max;
     p.routed = to_bank(routed);
-    p.a_sh = a_sh; p.a_sh_scale = a_sh_scale; p.S = has_sh ? S : 0; p.has_shared = has_sh;
+    p.a_sh = a_sh; p.a_sh_scale = (const float*)a_sh_scale; p.S = has_sh ? S : 0; p.has_shared = has_sh;
     p.shared = to_bank(shared);
     p.H = H; p.I = I; p.y = y; p.y_sh = y_sh; p.y_bf16 = (y_dt == MOE_BF16);
     p.y_e4m3 = (y_dt == MOE_E4M3); p.y_scale = y_scale; p.y_sh_bf16 = (y_sh_dt == MOE_BF16);
@@ -236,8 +255,9 @@ LayerWs layer_ws(int T, int H, int E, int k, int I, int x_dt, int w_dt, int has_
     L.src = take(R * 4);
     L.dest = take(R * 4);
     L.perm = take(moe::permute_ws_bytes((int)R, E));
-    L.xq = take(w_dt == MOE_E4M3 ? (size_t)T * H : 0);
-    L.xs = take(w_dt == MOE_E4M3 ? (size_t)T * (H / 128) * 4 : 0);
+    const bool q8 = w_dt == MOE_E4M3 || w_dt == MOE_MXFP4;               // x quantised in-layer
+    L.xq = take(q8 ? (size_t)T * H : 0);
+    L.xs = take(q8 ? (w_dt == MOE_E4M3 ? (size_t)T * (H / 128) * 4 : (size_t)T * (H / 32)) : 0);
     L.yperm = take(R * H * ypb);
     L.yscale = take(y_dt == MOE_E4M3 ? R * (H / 128) * 4 : 0);
     L.ysh = take(has_sh ? (size_t)T * H * yb : 0);
@@ -266,7 +286,8 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
     if (shared && (st = check_bank(shared, 1, H, I, "shared"))) return st;
     const int wdt = routed->dt;
     if (shared && shared->dt != wdt) return fail(MOE_ERR_UNSUPPORTED, "layer: shared/routed dtype differ");
-    const bool ok_combo = (x_dt == MOE_F32 && wdt == MOE_F32) || (x_dt == MOE_BF16 && (wdt == MOE_BF16 || wdt == MOE_E4M3));
+    const bool ok_combo = (x_dt == MOE_F32 && wdt == MOE_F32) ||
+                          (x_dt == MOE_BF16 && (wdt == MOE_BF16 || wdt == MOE_E4M3 || wdt == MOE_MXFP4));
     if (!ok_combo) return fail(MOE_ERR_UNSUPPORTED, "layer: x dtype %d with weights %d", x_dt, wdt);
     if (out_dt != MOE_F32 && out_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "layer: out dtype %d", out_dt);
     if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "layer: y dtype %d", y_dt);
@@ -298,6 +319,10 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
         e = moe::launch_quant_e4m3(x, 1, T, H, w8 + L.xq, (float*)(w8 + L.xs), s);
         a = w8 + L.xq;
         as = (const float*)(w8 + L.xs);
+    } else if (e == hipSuccess && wdt == MOE_MXFP4) {
+        e = moe::launch_quant_mxfp8(x, 1, T, H, w8 + L.xq, w8 + L.xs, s);
+        a = w8 + L.xq;
+        as = (const float*)(w8 + L.xs);   // E8M0 bytes [T][H/32]
     }
     if (e == hipSuccess) {
         moe::GffnProblem p{};

@@ -47,6 +47,22 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// ---- OCP MX (microscaling) block exponents ----------------------------------
+// A block of 32 values shares the scale 2^(E-127) (E8M0).  Per the OCP MX
+// conversion rule E - 127 = floor(log2(amax)) - emax_elem, clamped to the
+// E8M0 range; emax_elem = 8 for FP8 E4M3 elements (448 = 1.75 * 2^8).  For a
+// normal amax, floor(log2(amax)) is its exponent field minus 127, so
+// E = exponent field - 8; a zero or subnormal amax gives E = 0.  Finite fp32
+// inputs keep E <= 246.
+__device__ __forceinline__ uint32_t mx_e8m0_for_e4m3(float amax) {
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+    return (uint32_t)max(ef - 8, 0);
+}
+
+// 2^(127 - E) as an fp32 number (exact and normal for E <= 253): values times
+// this factor are the block's elements before rounding.
+__device__ __forceinline__ float mx_inv_scale(uint32_t E) { return __uint_as_float((254u - E) << 23); }
+
 // ---- wave64 helpers ----------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -9,7 +9,8 @@
 //   class 1: 16 < m <= 256    weight-streaming tiles of 64 rows   (bf16)
 //   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
 //                             or 64-row LDS tiles (fp32 or H % 256 != 0)
-// (non-bf16 layers put every group in class 2).  One single-workgroup kernel
+// (fp32 and e4m3 layers put every group in class 2; MXFP4 layers use the
+// MX weight-streaming tiles of gffn_mx.hip: 16 rows for m <= 16, else 64).  One single-workgroup kernel
 // writes, per class, the list of (group, first row) m-tiles with the heaviest
 // groups first (longest-processing-time order); then each class's gate/up
 // kernel and down kernel run as persistent grids that walk their list (see
@@ -173,7 +174,11 @@ constexpr int kPromoteMin = 32;
 static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
     const int bm2 = use_big(dt, H, I, R_max, S) ? 256 : 64;
-    if (dt == DT_BF16) {
+    if (dt == DT_MXFP4) {
+        c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
+        c.mlo[1] = 16; c.mhi[1] = 1 << 30;  c.bm[1] = 64;
+        c.mlo[2] = 0;  c.mhi[2] = 0;        c.bm[2] = 64;   // unused
+    } else if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
@@ -250,12 +255,14 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     // phase 1 (all classes), then phase 2: a group's down tiles need all of its h
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
+        e = p.dt == DT_MXFP4 ? launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s)
+          : k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
                   : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
+        e = p.dt == DT_MXFP4 ? launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s)
+          : k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
                   : cs.bm[k] == 256 ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
     }
     return e;

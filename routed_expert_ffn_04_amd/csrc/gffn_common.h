@@ -6,7 +6,7 @@
 
 namespace moe {
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2, DT_MXFP4 = 3 };   // weight types (MXFP4: MXFP8 activations)
 
 template <int DT> struct Op;
 template <> struct Op<DT_F32> {
@@ -46,12 +46,13 @@ struct TileList {
 };
 
 struct GArgs {
+    // activation scales: fp32 [rows][H/128] (E4M3), or E8M0 bytes [rows][H/32] (MXFP8)
     const uint8_t* a; const float* a_scale; const int32_t* src; int src_div;
     const uint8_t* a_sh; const float* a_sh_scale;
     const int32_t* offsets; int G; int R_max; int S;
     Bank routed, shared;
     int H, I;
-    uint8_t* h; float* h_scale;        // [R_max + S][I], [R_max + S][I/128]
+    uint8_t* h; float* h_scale;        // [R_max + S][I], [R_max + S][I/128] (MXFP4: E8M0 bytes [..][I/32])
     void* y; void* y_sh; int y_bf16;   // routed outputs bf16 (else fp32 unless y_e4m3)
     int y_e4m3; float* y_scale;        // routed outputs as e4m3 + [R_max][H/128] scales (large fp8 tiles)
     int y_sh_bf16;                     // shared outputs bf16 (else fp32)
@@ -111,13 +112,15 @@ struct TileIter {
     __device__ void next() { t += stride; }
 };
 
-// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip).
+// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_stream_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_big_gateup(int dt, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_big_down(int dt, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 int device_cu_count();
 
 }  // namespace moe

@@ -1,0 +1,371 @@
+// Grouped expert FFN with MXFP4 expert weights (OCP Microscaling: E2M1
+// codes, two per byte, with one E8M0 exponent per 32 consecutive reduction
+// elements) and MXFP8 activations (E4M3 codes with E8M0 per 32).
+//
+// The pages run the MoE GEMMs of their Blackwell deployment in FP4 ("How
+// DeepSeek inference works", the FP8/FP4 lever of its deployment table; "The
+// 31-Millisecond Smoking Gun", the FP4 MoE backends): in the decode regime the
+// grouped GEMM streams every touched expert's weights once, so 4.25 bits per
+// weight instead of 8 (or 16) cuts the dominant HBM traffic.  gfx950 consumes
+// both formats natively: v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a
+// 16 x 128 FP8 tile by a 128 x 16 FP4 tile and applies one E8M0 exponent per
+// lane and 32-element K block to each operand, which is exactly the MX block.
+//
+// Operand layout of one MFMA (16 rows x 16 columns x 128 K), as measured on
+// gfx950 with one-hot operands: lane l serves row (or column) l % 16 with
+// lane group g = l / 16, and
+//   FP4 weight:      K 32g .. 32g+31 (16 bytes, lower K in the low nibble);
+//   FP8 activation:  K 16g .. 16g+15 (bytes 0-15) and 64+16g .. 64+16g+15
+//                    (bytes 16-31);
+//   E8M0 exponents:  the block of K 32g .. 32g+31 of both operands.
+// The weight operand is 16 contiguous bytes of an output-major weight row and
+// the activation operand two 16-byte pieces of a row, so both are read from
+// memory straight into registers (the weight never touches LDS); the
+// exponents of a step's four K blocks are one dword, from which each lane
+// shifts out its own byte.
+//
+// Like the bf16 streaming kernels (gffn_stream.hip): tiles of MB*16 rows x TN
+// columns x all of K, P k-steps of loads in flight per wave, waves split K
+// (KS) or N, partial sums meet in LDS.  The gate/up epilogue applies SwiGLU
+// and writes h as MXFP8 along I (the down projection's activation), the down
+// epilogue writes fp32 or bf16 outputs.  Rows past a group's end re-read its
+// last row and are never stored.
+#include "gffn_common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kNB = 2;   // 16-column blocks per wave
+
+__device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
+
+// The activation operand of lane group g: p = row + step K offset + 16 g;
+// bytes 0-15 from p, bytes 16-31 from p + 64.
+__device__ __forceinline__ i32x8 load_act(const uint8_t* p) {
+    const i32x4 lo = *(const i32x4*)p, hi = *(const i32x4*)(p + 64);
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// D += A(fp8, exponents ea) x B(fp4, exponents eb); the low byte of ea / eb
+// is this lane's E8M0 (operand formats: 0 = FP8 E4M3, 4 = FP4 E2M1).
+__device__ __forceinline__ f32x4 mma_f8f4(i32x8 a, i32x4 b, f32x4 c, uint32_t ea, uint32_t eb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, widen(b), c, 0, 4, 0, (int)ea, 0, (int)eb);
+}
+
+// Activation row of tile row r (clamped into the group) for the gate/up phase.
+__device__ __forceinline__ void act_row(const GArgs& A, const GroupInfo& gi, int r, const uint8_t*& base,
+                                        const uint8_t*& ebase, long& ar) {
+    if (gi.shared) {
+        ar = r;
+        base = A.a_sh;
+        ebase = (const uint8_t*)A.a_sh_scale;
+    } else {
+        const int pp = gi.p0 + r;
+        ar = A.src ? A.src[pp] / A.src_div : pp;
+        base = A.a;
+        ebase = (const uint8_t*)A.a_scale;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- gate / up
+template <int MB, int KS, int P>
+__global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
+    constexpr int NW = 4 / KS;                 // waves along N
+    constexpr int TN = NW * kNB * 16;          // h columns per tile (a multiple of 32)
+    constexpr int RS = 2 * TN + 1;
+    const int H = A.H, I = A.I;
+    const int ntn = I / TN;
+    const int nsteps = H / 128 / KS;           // k-steps of 128 per wave
+
+    __shared__ float red[KS][16 * MB][RS];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int kw = wave % KS, nw = wave / KS;
+    const int kq = lane / 16;                  // K block of this lane within a step
+    const uint32_t esh = 8u * kq;              // its exponent byte within the step's dword
+
+    for (TileIter it(L, ntn); it.valid(); it.next()) {
+        const int t = (int)it.t;
+        __syncthreads();   // the previous tile's epilogue is done with `red`
+        const int2 tl = L.entries[t / ntn];
+        const GroupInfo gi = group_info(A, tl.x);
+        const int m0 = tl.y;
+        const int nt0 = (t % ntn) * TN;
+        const int n0 = nt0 + nw * kNB * 16;
+        const Bank bk = gi.shared ? A.shared : A.routed;
+        const int k0 = kw * nsteps * 128;
+
+        const uint8_t* ap[MB];
+        const uint8_t* aep[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const uint8_t *base, *ebase;
+            long ar;
+            act_row(A, gi, min(m0 + i * 16 + lane % 16, gi.m - 1), base, ebase, ar);
+            ap[i] = base + (size_t)ar * H + k0 + kq * 16;
+            aep[i] = ebase + (size_t)ar * (H / 32) + k0 / 32;
+        }
+        const uint8_t *gp[kNB], *up[kNB], *gep[kNB], *uep[kNB];
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            const size_t row = (size_t)gi.e * I + n0 + c * 16 + lane % 16;
+            gp[c] = (const uint8_t*)bk.wg + row * (H / 2) + (k0 + kq * 32) / 2;
+            up[c] = (const uint8_t*)bk.wu + row * (H / 2) + (k0 + kq * 32) / 2;
+            gep[c] = (const uint8_t*)bk.sg + row * (H / 32) + k0 / 32;
+            uep[c] = (const uint8_t*)bk.su + row * (H / 32) + k0 / 32;
+        }
+
+        f32x4 accg[MB][kNB], accu[MB][kNB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) accg[i][c] = accu[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        i32x8 ra[P][MB];
+        uint32_t rae[P][MB];
+        i32x4 rg[P][kNB], ru[P][kNB];
+        uint32_t rge[P][kNB], rue[P][kNB];
+        auto load = [&](int p, int step) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                rg[p][c] = *(const i32x4*)(gp[c] + step * 64);
+                ru[p][c] = *(const i32x4*)(up[c] + step * 64);
+                rge[p][c] = *(const uint32_t*)(gep[c] + step * 4);
+                rue[p][c] = *(const uint32_t*)(uep[c] + step * 4);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                ra[p][i] = load_act(ap[i] + step * 128);
+                rae[p][i] = *(const uint32_t*)(aep[i] + step * 4);
+            }
+        };
+        auto mma = [&](int p) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const uint32_t ea = rae[p][i] >> esh;
+                    accg[i][c] = mma_f8f4(ra[p][i], rg[p][c], accg[i][c], ea, rge[p][c] >> esh);
+                    accu[i][c] = mma_f8f4(ra[p][i], ru[p][c], accu[i][c], ea, rue[p][c] >> esh);
+                }
+        };
+        // ring of P k-steps in flight over the largest multiple of P, then
+        // the remaining steps one at a time
+        const int nmain = nsteps / P * P;
+        if (nmain > 0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) load(p, p);
+            for (int s0 = 0; s0 < nmain - P; s0 += P) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    mma(p);
+                    load(p, s0 + P + p);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < P; ++p) mma(p);
+        }
+        for (int s = nmain; s < nsteps; ++s) {
+            load(0, s);
+            mma(0);
+        }
+
+        // partial sums -> LDS; row = i*16 + 4*(lane/16) + q, col = nw*32 + c*16 + lane%16
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = i * 16 + 4 * (lane / 16) + q;
+                    const int col = nw * kNB * 16 + c * 16 + lane % 16;
+                    red[kw][row][col] = accg[i][c][q];
+                    red[kw][row][TN + col] = accu[i][c][q];
+                }
+        __syncthreads();
+        // SwiGLU, then MXFP8 along I: a thread takes 4 adjacent columns, so
+        // the 8 threads of one 32-column block are 8 adjacent lanes (TN is a
+        // multiple of 32 and the loop bound a multiple of 8: whole blocks
+        // enter or leave the loop together).
+        constexpr int TQ = TN / 4;
+        uint8_t* he = (uint8_t*)A.h_scale;
+        for (int e = tid; e < 16 * MB * TQ; e += 256) {
+            const int row = e / TQ, c4 = (e % TQ) * 4;
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < KS; ++w) {
+                    g += red[w][row][c4 + j];
+                    u += red[w][row][TN + c4 + j];
+                }
+                hv[j] = silu_mul(g, u);
+            }
+            float amax = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+            const uint32_t E = mx_e8m0_for_e4m3(amax);
+            const float f = mx_inv_scale(E);
+            const uint32_t code = f32x4_to_e4m3x4(hv[0] * f, hv[1] * f, hv[2] * f, hv[3] * f);
+            const int r = m0 + row;
+            if (r < gi.m) {
+                const int hr = h_row(A, gi, r);
+                *(uint32_t*)(A.h + (size_t)hr * I + nt0 + c4) = code;
+                if ((c4 & 31) == 0) he[(size_t)hr * (I / 32) + (nt0 + c4) / 32] = (uint8_t)E;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- down
+template <int MB, int P>
+__global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
+    constexpr int TN = 4 * kNB * 16;           // output (H) columns per tile; each wave all of K
+    constexpr int RS = TN + 1;
+    const int H = A.H, I = A.I;
+    const int ntn = H / TN;
+    const int nsteps = I / 128;
+
+    __shared__ float red[16 * MB][RS];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int kq = lane / 16;
+    const uint32_t esh = 8u * kq;
+    const uint8_t* he = (const uint8_t*)A.h_scale;
+
+    for (TileIter it(L, ntn); it.valid(); it.next()) {
+        const int t = (int)it.t;
+        __syncthreads();
+        const int2 tl = L.entries[t / ntn];
+        const GroupInfo gi = group_info(A, tl.x);
+        const int m0 = tl.y;
+        const int nt0 = (t % ntn) * TN;
+        const int n0 = nt0 + wave * kNB * 16;
+        const Bank bk = gi.shared ? A.shared : A.routed;
+
+        const uint8_t* ap[MB];
+        const uint8_t* aep[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int hr = h_row(A, gi, min(m0 + i * 16 + lane % 16, gi.m - 1));
+            ap[i] = A.h + (size_t)hr * I + kq * 16;
+            aep[i] = he + (size_t)hr * (I / 32);
+        }
+        const uint8_t *dp[kNB], *dep[kNB];
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            const size_t row = (size_t)gi.e * H + n0 + c * 16 + lane % 16;
+            dp[c] = (const uint8_t*)bk.wd + row * (I / 2) + kq * 16;
+            dep[c] = (const uint8_t*)bk.sd + row * (I / 32);
+        }
+
+        f32x4 acc[MB][kNB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        i32x8 ra[P][MB];
+        uint32_t rae[P][MB];
+        i32x4 rd[P][kNB];
+        uint32_t rde[P][kNB];
+        auto load = [&](int p, int step) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                rd[p][c] = *(const i32x4*)(dp[c] + step * 64);
+                rde[p][c] = *(const uint32_t*)(dep[c] + step * 4);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                ra[p][i] = load_act(ap[i] + step * 128);
+                rae[p][i] = *(const uint32_t*)(aep[i] + step * 4);
+            }
+        };
+        auto mma = [&](int p) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[i][c] = mma_f8f4(ra[p][i], rd[p][c], acc[i][c], rae[p][i] >> esh, rde[p][c] >> esh);
+        };
+        const int nmain = nsteps / P * P;
+        if (nmain > 0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) load(p, p);
+            for (int s0 = 0; s0 < nmain - P; s0 += P) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    mma(p);
+                    load(p, s0 + P + p);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < P; ++p) mma(p);
+        }
+        for (int s = nmain; s < nsteps; ++s) {
+            load(0, s);
+            mma(0);
+        }
+
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[i * 16 + 4 * (lane / 16) + q][wave * kNB * 16 + c * 16 + lane % 16] = acc[i][c][q];
+        __syncthreads();
+        void* yb = gi.shared ? A.y_sh : A.y;
+        const int ybf = gi.shared ? A.y_sh_bf16 : A.y_bf16;
+        for (int e = tid; e < 16 * MB * TN; e += 256) {
+            const int row = e / TN, col = e % TN;
+            const int r = m0 + row;
+            if (r >= gi.m) continue;
+            const float v = red[row][col];
+            const size_t yr = gi.shared ? (size_t)r : (size_t)(gi.p0 + r);
+            if (ybf) ((uint16_t*)yb)[yr * H + nt0 + col] = (uint16_t)f32_to_bf16_bits(v);
+            else ((float*)yb)[yr * H + nt0 + col] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <class K>
+static int mx_persistent_grid(K kernel) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    return per_cu * device_cu_count();
+}
+
+#define MOE_MX_LAUNCH(KERNEL)                                                       \
+    do {                                                                            \
+        static const int g = mx_persistent_grid(KERNEL);                            \
+        hipLaunchKernelGGL(KERNEL, dim3(g), dim3(256), 0, s, A, L);                 \
+    } while (0)
+
+// The K split of gate/up over two waves needs an even number of 128-wide
+// k-steps (H % 256 == 0); otherwise every wave covers all of K.  Tiles of 16
+// rows keep 4 k-steps of loads in flight, tiles of 64 rows 2 (registers).
+hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
+    const bool split = (A.H / 128) % 2 == 0;
+    if (mb == 1) {
+        if (split) MOE_MX_LAUNCH((mx_gateup_kernel<1, 2, 4>)); else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, 4>));
+    } else {
+        if (split) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2>)); else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2>));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
+    if (mb == 1) MOE_MX_LAUNCH((mx_down_kernel<1, 4>));
+    else MOE_MX_LAUNCH((mx_down_kernel<4, 2>));
+    return hipGetLastError();
+}
+#undef MOE_MX_LAUNCH
+
+}  // namespace moe

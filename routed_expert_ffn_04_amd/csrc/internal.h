@@ -22,6 +22,8 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int
 // quant.hip
 hipError_t launch_quant_e4m3(const void* x, int x_bf16, int rows, int cols, uint8_t* q,
                              float* scale, hipStream_t s);
+hipError_t launch_quant_mxfp8(const void* x, int x_bf16, int rows, int cols, uint8_t* q,
+                              uint8_t* e8, hipStream_t s);
 
 // combine.hip
 // y_mode: 0 fp32, 1 bf16, 2 e4m3 codes + y_scale [rows][H/128]
@@ -36,8 +38,9 @@ struct Bank {
 };
 
 struct GffnProblem {
-    int dt;                       // 0 f32, 1 bf16, 2 e4m3 (activations and weights)
-    const void* a; const float* a_scale; const int32_t* src; int src_div;
+    int dt;                       // 0 f32, 1 bf16, 2 e4m3 (activations and weights),
+                                  // 3 MXFP4 weights with MXFP8 activations
+    const void* a; const float* a_scale; const int32_t* src; int src_div;   // a_scale: E8M0 bytes for MXFP8
     const int32_t* offsets; int G; int R_max;
     Bank routed;
     const void* a_sh; const float* a_sh_scale; int S; int has_shared;

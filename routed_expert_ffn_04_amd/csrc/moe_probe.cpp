@@ -4,6 +4,7 @@
 //   moe_probe decode  [iters]   T=128,   H=7168, 256+1 experts, I=2048, top-8, bf16, fp32 out
 //   moe_probe skew    [iters]   T=4096,  same layer, additive logit bias on 20 experts
 //   moe_probe prefill [iters]   T=16384, same layer with e4m3 block-scaled weights, bf16 out
+//   moe_probe decode-mxfp4 [iters]  the decode layer with MXFP4 expert weights
 //   moe_probe copy    [iters]   a plain device copy of 1 GiB (counter calibration)
 //   moe_probe file DIR [iters]  the workload described by DIR/meta.txt (written by
 //                               bench.py --dump-inputs): a layer with the dumped
@@ -80,6 +81,12 @@ __global__ void fill_e4m3(uint8_t* p, size_t n, uint64_t seed) {
     }
 }
 
+// bytes lo + (hash % span): E2M1 code pairs (0, 256) or E8M0 exponents
+__global__ void fill_u8(uint8_t* p, size_t n, uint64_t seed, uint32_t lo, uint32_t span) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = (uint8_t)(lo + hash32(seed * 0x9E3779B97F4A7C15ull + i) % span);
+}
+
 __global__ void copy_u4(const uint4* __restrict__ s, uint4* __restrict__ d, size_t n) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         d[i] = s[i];
@@ -99,10 +106,21 @@ static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
     BankBuf b{};
     const size_t ne = (size_t)n * H * I;
     const size_t eb = dt == MOE_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
-    void* g = dalloc(ne * eb);
-    void* u = dalloc(ne * eb);
-    void* w = dalloc(ne * eb);
-    if (dt == MOE_E4M3) {
+    const size_t nb = dt == MOE_MXFP4 ? ne / 2 : ne * eb;
+    void* g = dalloc(nb);
+    void* u = dalloc(nb);
+    void* w = dalloc(nb);
+    if (dt == MOE_MXFP4) {
+        // uniform E2M1 codes, exponents 2^-8 / 2^-7 (weights of rms about 0.018)
+        uint8_t* e[3];
+        for (int j = 0; j < 3; ++j) {
+            hipLaunchKernelGGL(fill_u8, dim3(4096), dim3(256), 0, 0, (uint8_t*)(j == 0 ? g : j == 1 ? u : w), nb,
+                               seed + 1 + j, 0u, 256u);
+            e[j] = (uint8_t*)dalloc(ne / 32);
+            hipLaunchKernelGGL(fill_u8, dim3(4096), dim3(256), 0, 0, e[j], ne / 32, seed + 11 + j, 119u, 2u);
+        }
+        b.d.s_gate = e[0]; b.d.s_up = e[1]; b.d.s_down = e[2];
+    } else if (dt == MOE_E4M3) {
         hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)g, ne, seed + 1);
         hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)u, ne, seed + 2);
         hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)w, ne, seed + 3);
@@ -156,7 +174,9 @@ static void* load_file(const std::string& path, size_t bytes) {
     return d;
 }
 
-static int dt_of(const std::string& s) { return s == "f32" ? MOE_F32 : s == "bf16" ? MOE_BF16 : MOE_E4M3; }
+static int dt_of(const std::string& s) {
+    return s == "f32" ? MOE_F32 : s == "bf16" ? MOE_BF16 : s == "mxfp4" ? MOE_MXFP4 : MOE_E4M3;
+}
 
 int main(int argc, char** argv) {
     const std::string mode = argc > 1 ? argv[1] : "decode";
@@ -195,12 +215,16 @@ int main(int argc, char** argv) {
             std::istringstream gs(m["groups"]);
             for (int g; gs >> g;) offs.push_back(offs.back() + g);
             const int G = (int)offs.size() - 1, R = offs.back();
-            const size_t eb = dt == MOE_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
+            const bool q8 = dt == MOE_E4M3 || dt == MOE_MXFP4;
+            const size_t eb = q8 ? 1 : dt == MOE_BF16 ? 2 : 4;
             void* a = dalloc((size_t)(R + S) * H * eb);
-            float* as = (float*)dalloc((size_t)(R + S) * (H / 128) * 4);
-            if (dt == MOE_E4M3) hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)a, (size_t)(R + S) * H, 21);
+            float* as = (float*)dalloc((size_t)(R + S) * (H / 128) * 4);   // also holds [R+S][H/32] E8M0 bytes
+            if (q8) hipLaunchKernelGGL(fill_e4m3, dim3(4096), dim3(256), 0, 0, (uint8_t*)a, (size_t)(R + S) * H, 21);
             else hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, (uint16_t*)a, (size_t)(R + S) * H, 21, 1.73f);
-            hipLaunchKernelGGL(fill_f32, dim3(256), dim3(256), 0, 0, as, (size_t)(R + S) * (H / 128), 22, 1e-2f);
+            if (dt == MOE_MXFP4)
+                hipLaunchKernelGGL(fill_u8, dim3(256), dim3(256), 0, 0, (uint8_t*)as, (size_t)(R + S) * (H / 32), 22, 118u, 4u);
+            else
+                hipLaunchKernelGGL(fill_f32, dim3(256), dim3(256), 0, 0, as, (size_t)(R + S) * (H / 128), 22, 1e-2f);
             int32_t* d_offs = (int32_t*)dalloc(offs.size() * 4);
             CK(hipMemcpy(d_offs, offs.data(), offs.size() * 4, hipMemcpyHostToDevice));
             BankBuf routed = make_bank(G, H, I, dt, 100);
@@ -211,9 +235,11 @@ int main(int argc, char** argv) {
             void* ws = dalloc(wsb);
             CK(hipDeviceSynchronize());
             auto run = [&]() {
-                CM(moe_grouped_ffn(a, dt, dt == MOE_E4M3 ? as : nullptr, nullptr, 1, d_offs, G, R, &routed.d,
-                                   S > 0 ? (const uint8_t*)a + (size_t)R * H * eb : nullptr,
-                                   (S > 0 && dt == MOE_E4M3) ? as + (size_t)R * (H / 128) : nullptr, S,
+                const void* ash = !q8 || S == 0 ? nullptr
+                                : dt == MOE_MXFP4 ? (const void*)((const uint8_t*)as + (size_t)R * (H / 32))
+                                                  : (const void*)(as + (size_t)R * (H / 128));
+                CM(moe_grouped_ffn(a, dt == MOE_MXFP4 ? MOE_MXFP8 : dt, q8 ? as : nullptr, nullptr, 1, d_offs, G, R, &routed.d,
+                                   S > 0 ? (const uint8_t*)a + (size_t)R * H * eb : nullptr, ash, S,
                                    S > 0 ? &shared.d : nullptr, y, MOE_BF16, nullptr, S > 0 ? y_sh : nullptr, MOE_BF16,
                                    ws, wsb, st));
             };
@@ -234,6 +260,7 @@ int main(int argc, char** argv) {
     if (mode == "decode") { T = 128; w_dt = MOE_BF16; out_dt = MOE_F32; }
     else if (mode == "skew") { T = 4096; w_dt = MOE_BF16; out_dt = MOE_F32; bias = true; }
     else if (mode == "prefill") { T = 16384; w_dt = MOE_E4M3; out_dt = MOE_BF16; }
+    else if (mode == "decode-mxfp4") { T = 128; w_dt = MOE_MXFP4; out_dt = MOE_F32; }
     else if (mode != "file") { fprintf(stderr, "unknown mode %s\n", mode.c_str()); return 1; }
     int H = 7168, E = 256, k = 8, I = 2048, score = MOE_SIGMOID, has_shared = 1, y_dt = -1;
     void* x = nullptr;

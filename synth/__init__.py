@@ -414,3 +414,24 @@ def config(cid: int, device="cpu", T: Optional[int] = None) -> Workload:
         return make_layer(T or 16384, 7168, 256, 8, 2048, x_dt="bf16", w_dt="e4m3", out_dt="bf16",
                           score="sigmoid", shared=True, layer_seed=2, x_seed=5, device=device, name=name)
     raise ValueError(cid)
+
+
+def mxfp4_name(cid: int) -> str:
+    """Name of layer workload cid with MXFP4 expert weights."""
+    return CONFIG_NAMES[cid].replace("-bf16-", "-mxfp4-").replace("-fp8-", "-mxfp4-")
+
+
+def config_mxfp4(cid: int, device="cpu", T: Optional[int] = None) -> Workload:
+    """Layer workload cid (2, 3 or 5) with MXFP4 expert weights in place of
+    its bf16 / e4m3 ones: the same tokens, router, bias and so the same
+    routing; random MXFP4 banks (see _bank_mxfp4); x arrives in bf16 and is
+    quantised to MXFP8 in-layer."""
+    if cid not in (2, 3, 5):
+        raise ValueError(f"MXFP4 variants exist for the layer workloads 2, 3 and 5, not {cid}")
+    r = routing_inputs(cid, device="cpu")
+    T = T or r["T"]
+    ls = 2
+    wl = make_layer(T, r["H"], r["E"], r["k"], r["I"], x_dt="bf16", w_dt="mxfp4", out_dt=r["out_dt"],
+                    score=r["score"], shared=r["shared"], bias=r["bias"], layer_seed=ls,
+                    x_seed={2: 2, 3: 3, 5: 5}[cid], device=device, name=mxfp4_name(cid))
+    return wl

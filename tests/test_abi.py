@@ -18,7 +18,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ["moe_route", "moe_permute", "moe_quant_e4m3_1x128", "moe_grouped_ffn", "moe_combine", "moe_layer"]:
+    for n in ["moe_route", "moe_permute", "moe_quant_e4m3_1x128", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_combine",
+              "moe_layer"]:
         assert n in names
 
 
@@ -45,6 +46,11 @@ def test_workspace_queries_are_host_only():
     c = L.moe_layer_workspace_size(16384, 7168, 256, 8, 2048, 1, 2, 1, 1, 2)
     R = 16384 * 8
     assert b - c >= R * 7168 - R * 56 * 4 - 4096
+    # MXFP4 layer: x and h as MXFP8 (codes + one byte per 32 values) take as
+    # many bytes as the e4m3 layer's codes with fp32 scales per 128 (the tile
+    # lists differ by a few entries)
+    m = L.moe_layer_workspace_size(128, 7168, 256, 8, 2048, 1, 3, 1, 0, 0)
+    assert abs(m - L.moe_layer_workspace_size(128, 7168, 256, 8, 2048, 1, 2, 1, 0, 0)) <= 1 << 16
 
 
 P = 0x1000  # a non-null dummy address; validation fails before any use
@@ -82,10 +88,14 @@ def test_permute_and_combine_validation():
     assert L.moe_combine(P, 2, P, P, 2, P, P, 4, 2, 128, P, 0, None) == moe.MOE_ERR_UNSUPPORTED     # e4m3 y_sh
     assert L.moe_quant_e4m3_1x128(P, 1, 4, 100, P, P, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_quant_e4m3_1x128(None, 1, 0, 128, None, None, None) == moe.MOE_OK
+    assert L.moe_quant_mxfp8(P, 1, 4, 48, P, P, None) == moe.MOE_ERR_UNSUPPORTED      # cols % 32
+    assert L.moe_quant_mxfp8(P, 2, 4, 64, P, P, None) == moe.MOE_ERR_UNSUPPORTED      # e4m3 input
+    assert L.moe_quant_mxfp8(P, 1, 4, 64, P, None, None) == moe.MOE_ERR_INVALID       # no exponent output
+    assert L.moe_quant_mxfp8(None, 1, 0, 64, None, None, None) == moe.MOE_OK
 
 
 def _bank(n, H, I, dt, scales=True):
-    s = P if (dt == moe.E4M3 and scales) else None
+    s = P if (dt in (moe.E4M3, moe.MXFP4) and scales) else None
     return moe.ExpertsT(n, H, I, dt, P, P, P, s, s, s)
 
 
@@ -106,6 +116,13 @@ def test_grouped_ffn_validation():
     assert call(moe.BF16, _bank(8, 200, 256, moe.BF16)) == moe.MOE_ERR_UNSUPPORTED
     assert call(moe.BF16, b, ws=16) == moe.MOE_ERR_WORKSPACE
     assert call(moe.BF16, b, sh=_bank(1, 256, 256, moe.E4M3)) == moe.MOE_ERR_UNSUPPORTED
+    mx4 = _bank(8, 256, 256, moe.MXFP4)
+    assert call(moe.E4M3, mx4, a_s=P) == moe.MOE_ERR_UNSUPPORTED              # MXFP4 weights take MXFP8 activations
+    assert call(moe.MXFP8, mx4) == moe.MOE_ERR_INVALID                        # ... with their exponents
+    assert call(moe.MXFP8, _bank(8, 256, 256, moe.MXFP4, scales=False), a_s=P) == moe.MOE_ERR_INVALID
+    assert call(moe.MXFP8, mx4, a_s=P + 2) == moe.MOE_ERR_INVALID            # exponents 4-byte aligned
+    assert call(moe.MXFP8, mx4, a_s=P, y_dt=2) == moe.MOE_ERR_UNSUPPORTED    # no e4m3 outputs from MXFP4
+    assert call(moe.MXFP8, mx4, a_s=P, ws=16) == moe.MOE_ERR_WORKSPACE       # valid up to the workspace
 
 
 def test_layer_validation():
@@ -119,3 +136,7 @@ def test_layer_validation():
     assert f(moe.BF16, b, ws=128) == moe.MOE_ERR_WORKSPACE
     assert f(moe.BF16, b, out_dt=2) == moe.MOE_ERR_UNSUPPORTED
     assert f(moe.BF16, b, y_dt=2) == moe.MOE_ERR_UNSUPPORTED    # fp8 combine needs e4m3 weights
+    m4 = _bank(8, 256, 256, moe.MXFP4)
+    assert f(moe.F32, m4) == moe.MOE_ERR_UNSUPPORTED            # MXFP4 layers take bf16 x
+    assert f(moe.BF16, m4, y_dt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert f(moe.BF16, m4, ws=128) == moe.MOE_ERR_WORKSPACE     # valid up to the workspace

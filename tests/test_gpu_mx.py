@@ -1,0 +1,113 @@
+"""GPU parity of the MXFP4 path (E2M1 expert weights with E8M0 per-32
+exponents, MXFP8 activations and h) against the CPU oracle.
+
+Bit-exact: MXFP8 codes and exponents of the activation quantisation.
+Expert and layer outputs: rel-Frobenius <= 3e-2 (the fp8 bar; the weights and
+activations are exact on both sides, so the residual is fp32 accumulation
+and the few h elements whose rounding decision flips between fp32 and the
+oracle's fp64)."""
+import numpy as np
+import pytest
+import torch
+
+import routed_expert_ffn_04_amd as moe
+import synth
+from oracle import mx
+from oracle import moe as om
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL_FROB_FP8 = 3e-2
+
+
+def rel_frob(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_out(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape and np.isfinite(got).all(), what
+    rf = rel_frob(got, ref)
+    print(f"[{what}] rel_frob={rf:.3e} max_abs={np.abs(got - ref).max():.3e} max|ref|={np.abs(ref).max():.3e}",
+          flush=True)
+    assert rf <= TOL_FROB_FP8, what
+
+
+@pytest.mark.parametrize("rows,cols,x_dt", [(1, 32, "bf16"), (37, 7168, "bf16"), (64, 256, "f32"), (1000, 96, "bf16")])
+def test_quant_mxfp8_bit_exact(rows, cols, x_dt):
+    print(f"quant_mxfp8 rows={rows} cols={cols} {x_dt}", flush=True)
+    x = synth.normal((rows, cols), rows + 5, 7, 1.0, torch.float32 if x_dt == "f32" else torch.bfloat16)
+    x[0, :32] = 0                                  # all-zero block: E = 0, codes 0
+    if rows > 3:
+        x[1, 5] = -1e-6                            # rounds to -0 (code 0x80) at its block's scale
+        x[2, 32:64] *= 1e4                         # large magnitudes
+        x[3, 0:32] = 1.99                          # amax in (448 X, 512 X): saturates to 448 X
+        if x_dt == "f32":
+            x[3, 32:64] = 2.0 ** -132              # below 2^-127: E clamps to 0
+    q_ref, e_ref = mx.mx_quant(x.float().numpy(), "e4m3")
+    q, e = moe.quant_mxfp8(x.to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(e.cpu().numpy(), e_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+GROUPED_CASES = [
+    # group rows (0 = empty expert), shared rows, H, I
+    ([130, 5, 0, 64, 1], 40, 256, 256),        # 16-row and 64-row tiles, a ragged 130
+    ([3, 77, 200], 0, 384, 512),               # odd number of 128-wide k-steps (no K split)
+    ([16, 17, 2], 33, 512, 384),               # class boundaries; odd k-steps in the down projection
+]
+
+
+@pytest.mark.parametrize("gm,sm,H,I", GROUPED_CASES)
+@pytest.mark.parametrize("y_dt", ["f32", "bf16"])
+def test_grouped_ffn_mxfp4_parity(gm, sm, H, I, y_dt):
+    print(f"grouped mxfp4 gm={gm} sm={sm} H={H} I={I} y={y_dt}", flush=True)
+    wl = synth.make_grouped(gm, sm, H, I, dt="mxfp4", seed=sum(gm) + sm + 1, y_dt=y_dt)
+    ref = om.grouped_ffn(wl)
+    R = int(sum(gm))
+    x = wl.x.to(DEV)
+    a, a_e = moe.quant_mxfp8(x)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(gm)]), dtype=torch.int32, device=DEV)
+    routed = moe.Experts.from_bank(wl.routed.to(DEV))
+    shared = moe.Experts.from_bank(wl.shared.to(DEV)) if sm else None
+    ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
+    y, y_sh = moe.grouped_ffn(a, offs, routed, a_scale=a_e, R_max=R,
+                              a_sh=a[R:] if sm else None, a_sh_scale=a_e[R:] if sm else None,
+                              shared=shared, y_dtype=ydt)
+    torch.cuda.synchronize()
+    yc = y.float().cpu().numpy()
+    starts = np.concatenate([[0], np.cumsum(gm)])
+    for g in range(len(gm)):
+        if gm[g]:
+            check_out(yc[starts[g]:starts[g + 1]], ref[g][1], f"group {g}")
+    if sm:
+        check_out(y_sh.float().cpu().numpy(), ref["shared"][1], "shared")
+
+
+LAYER_CASES = [
+    dict(T=100, H=512, E=32, k=4, I=256, out_dt="f32", score="sigmoid", shared=True),
+    dict(T=37, H=384, E=16, k=3, I=384, out_dt="bf16", score="softmax", shared=True),
+    dict(T=150, H=256, E=8, k=2, I=256, out_dt="f32", score="sigmoid", shared=False),
+]
+
+
+@pytest.mark.parametrize("cfg", LAYER_CASES, ids=lambda c: f"T{c['T']}-H{c['H']}-E{c['E']}")
+def test_layer_mxfp4_parity(cfg):
+    print(f"layer mxfp4 {cfg}", flush=True)
+    c = dict(cfg)
+    wl = synth.make_layer(c.pop("T"), c.pop("H"), c.pop("E"), c.pop("k"), c.pop("I"), w_dt="mxfp4",
+                          seed=321, **c)
+    ref = om.moe_layer(wl)
+    f = lambda t: None if t is None else t.to(DEV)
+    out, ids, w, counts = moe.layer(f(wl.x), f(wl.w_router), f(wl.bias), wl.k, wl.score,
+                                    moe.Experts.from_bank(wl.routed.to(DEV)),
+                                    moe.Experts.from_bank(wl.shared.to(DEV)) if wl.shared is not None else None,
+                                    out_dtype=torch.float32 if wl.out_dt == "f32" else torch.bfloat16,
+                                    want_routing=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    check_out(out.float().cpu().numpy(), ref["out"], "layer")
