@@ -30,14 +30,16 @@ import synth  # noqa: E402
 
 METRIC = "MoE layer tokens/s at 1 GPU; grouped-FFN HBM GB/s (T=128) and MFMA TFLOPS (T=16384)"
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3,
+               # fp8 x fp4 scaled MFMA: priced at the fp8 dense peak (the fp4 x fp4 rate is 10.1 PF)
+               "mxfp4": 5000.0}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False):
+def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False, mxfp4: bool = False):
     """Write what decides the work of a workload (for the native probe that
     hardware-counter runs use): the tokens, router and bias of a layer
     (routing depends on nothing else), or the group sizes of the pre-routed
@@ -56,6 +58,8 @@ def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False):
                     bias=int(wl["bias"] is not None))
         if fp8_combine:
             meta["y_dt"] = "e4m3"
+        if mxfp4:
+            meta["w_dt"] = "mxfp4"
         wl["x"].contiguous().view(torch.uint8).numpy().tofile(os.path.join(out_dir, "x.bin"))
         wl["w_router"].contiguous().numpy().tofile(os.path.join(out_dir, "w_router.bin"))
         if wl["bias"] is not None:
@@ -83,9 +87,9 @@ def measured_traffic(name: str):
     return None if w is None else int(w["bytes"])
 
 
-def build_inputs(cid: int, dev):
+def build_inputs(cid: int, dev, mxfp4: bool = False):
     t0 = time.time()
-    wl = synth.config(cid, device=dev)
+    wl = synth.config_mxfp4(cid, device=dev) if mxfp4 else synth.config(cid, device=dev)
     torch.cuda.synchronize()
     log(f"config {cid} ({wl.name}) generated on {dev} in {time.time() - t0:.1f}s")
     return wl
@@ -101,6 +105,7 @@ class LayerRunner:
         self.routed = moe.Experts.from_bank(wl.routed)
         self.shared = moe.Experts.from_bank(wl.shared) if wl.shared is not None else None
         self.fp8 = wl.w_dt == "e4m3"
+        self.mx = wl.w_dt == "mxfp4"              # x quantised to MXFP8 in-layer
         ydt = torch.bfloat16 if wl.out_dt == "bf16" else torch.float32
         R = T * k
         L = moe.lib()
@@ -114,13 +119,14 @@ class LayerRunner:
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.src = torch.empty(R, dtype=torch.int32, device=dev)
         self.dest = torch.empty(R, dtype=torch.int32, device=dev)
-        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.fp8 else None
-        self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if (self.fp8 or self.mx) else None
+        self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.fp8 else \
+            torch.empty((T, H // 32), dtype=torch.uint8, device=dev) if self.mx else None
         self.y = torch.empty((R, H), dtype=torch.uint8 if fp8_combine else ydt, device=dev)
         self.y_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8_combine else None
         self.y_sh = torch.empty((T, H), dtype=ydt, device=dev) if self.shared else None
         self.out = torch.empty((T, H), dtype=ydt, device=dev)
-        self.names = ["route", "quant", "permute", "grouped_ffn", "combine"] if self.fp8 else \
+        self.names = ["route", "quant", "permute", "grouped_ffn", "combine"] if (self.fp8 or self.mx) else \
             ["route", "permute", "grouped_ffn", "combine"]
 
     def calls(self):
@@ -129,9 +135,11 @@ class LayerRunner:
                                          out=(self.ids, self.w))
         if self.fp8:
             yield "quant", lambda: moe.quant_e4m3_1x128(wl.x, out=(self.xq, self.xs))
+        if self.mx:
+            yield "quant", lambda: moe.quant_mxfp8(wl.x, out=(self.xq, self.xs))
         yield "permute", lambda: moe.permute(self.ids, wl.E, ws=self.ws_perm,
                                              out=(self.counts, self.offsets, self.src, self.dest))
-        a, a_s = (self.xq, self.xs) if self.fp8 else (wl.x, None)
+        a, a_s = (self.xq, self.xs) if (self.fp8 or self.mx) else (wl.x, None)
         yield "grouped_ffn", lambda: moe.grouped_ffn(
             a, self.offsets, self.routed, a_scale=a_s, src=self.src, src_div=wl.k, R_max=wl.T * wl.k,
             a_sh=a if self.shared else None, a_sh_scale=a_s if self.shared else None, shared=self.shared,
@@ -258,9 +266,14 @@ def main():
     ap.add_argument("--dump-inputs", metavar="DIR", help="write the workload's routing inputs for the native probe and exit")
     ap.add_argument("--fp8-combine", action="store_true",
                     help="routed expert outputs as e4m3 per 1x128 before the combine (fp8 layers)")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="the layer workload with MXFP4 expert weights (MXFP8 activations and h)")
     args = ap.parse_args()
+    if args.mxfp4 and (args.config not in (2, 3, 5) or args.fp8_combine):
+        print("bench.py: --mxfp4 applies to the layer workloads 2, 3 and 5 (without --fp8-combine)", file=sys.stderr)
+        sys.exit(2)
     if args.dump_inputs:
-        dump_inputs(args.config, args.dump_inputs, args.fp8_combine)
+        dump_inputs(args.config, args.dump_inputs, args.fp8_combine, args.mxfp4)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -272,7 +285,7 @@ def main():
     moe.lib()
     dev = torch.device("cuda:0")
     cid = args.config
-    wl = build_inputs(cid, dev)
+    wl = build_inputs(cid, dev, args.mxfp4)
     if args.fp8_combine and (cid == 4 or wl.w_dt != "e4m3"):
         print("bench.py: --fp8-combine applies to the fp8 layer workloads only", file=sys.stderr)
         sys.exit(2)
@@ -291,7 +304,7 @@ def main():
     else:
         group_rows = runner.counts.cpu().tolist()
         shared_rows = wl.T if wl.shared is not None else 0
-        a_dt = "e4m3" if wl.w_dt == "e4m3" else wl.x_dt
+        a_dt = {"e4m3": "e4m3", "mxfp4": "mxfp8"}.get(wl.w_dt, wl.x_dt)
         y_dt = wl.out_dt
     rows = sum(group_rows) + shared_rows
     flops = accounting.ffn_flops(rows, wl.H, wl.I)
@@ -328,7 +341,8 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"bf16": "bf16", "e4m3": "fp8-e4m3", "f32": "f32"}[wl.w_dt],
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "e4m3": "fp8-e4m3", "f32": "f32", "mxfp4": "mxfp4 x mxfp8"}[wl.w_dt],
         "data": "synthetic (seeded counter-based normals; random-init weights)", "config": cfg,
         "roofline": roof,
         "grouped_ffn": {"ms": round(gffn_ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)},

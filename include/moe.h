@@ -148,7 +148,7 @@ moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t 
 /* ---- grouped FFN --------------------------------------------------------
  * For every routed group g (expert g of `routed`) and permuted row p in
  * [offsets[g], offsets[g+1]):
- *     a_p = a[src[p] / src_div]   (a[p] when src is NULL)
+ *     a_p = a[src[p] / src_div]   (a[p] when src is NULL; src values in [0, R_max))
  *     h_p = silu(a_p W_gate) * (a_p W_up),   silu(z) = z / (1 + exp(-z))
  *     y[p] = round_y(h'_p W_down)
  * and, when `shared` is non-NULL, the same with the shared expert for the S

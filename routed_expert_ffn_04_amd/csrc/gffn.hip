@@ -171,12 +171,19 @@ static bool use_big(int dt, int H, int I, int R_max, int S) {
 
 constexpr int kPromoteMin = 32;
 
+// MXFP4: groups of up to this many rows take the 16-row streaming tiles
+// (several m-tiles of one group re-read its weights, mostly from L2).
+#ifndef MOE_MX_C0_MAX
+#define MOE_MX_C0_MAX 16
+#endif
+constexpr int kMxC0Max = MOE_MX_C0_MAX;
+
 static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
     const int bm2 = use_big(dt, H, I, R_max, S) ? 256 : 64;
     if (dt == DT_MXFP4) {
-        c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
-        c.mlo[1] = 16; c.mhi[1] = 1 << 30;  c.bm[1] = 64;
+        c.mlo[0] = 0;  c.mhi[0] = kMxC0Max; c.bm[0] = 16;
+        c.mlo[1] = kMxC0Max; c.mhi[1] = 1 << 30;  c.bm[1] = 64;
         c.mlo[2] = 0;  c.mhi[2] = 0;        c.bm[2] = 64;   // unused
     } else if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;

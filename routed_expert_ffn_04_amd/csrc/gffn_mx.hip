@@ -36,14 +36,38 @@ namespace moe {
 
 namespace {
 
-constexpr int kNB = 2;   // 16-column blocks per wave
+
+// Scheduling barriers that keep each step's refill loads right behind that
+// step's MFMAs.  Off: measured on MI355X, the compiler's own order (refills
+// gathered at the end of the ring, waits counted per step) streams ~40%
+// faster.
+#ifndef MOE_MX_PIN
+#define MOE_MX_PIN 0
+#endif
+__device__ __forceinline__ void pin() {
+#if MOE_MX_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
 
 __device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
 
+// Loads through global-address-space pointers: every operand lives in device
+// memory, and a load the compiler cannot place (a generic "flat" access)
+// would also count against the LDS counter and force full waits in the
+// software pipeline.
+template <class T>
+__device__ __forceinline__ T gld(const uint8_t* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+
 // The activation operand of lane group g: p = row + step K offset + 16 g;
-// bytes 0-15 from p, bytes 16-31 from p + 64.
+// bytes 0-15 from p, bytes 16-31 from p + 64.  Tile rows past the group's
+// end re-read its last row (their outputs are never stored); in the decode
+// regime most of a tile's 16 rows are such repeats, which cost little
+// (measured: masking them off with zero-filling buffer loads was slower).
 __device__ __forceinline__ i32x8 load_act(const uint8_t* p) {
-    const i32x4 lo = *(const i32x4*)p, hi = *(const i32x4*)(p + 64);
+    const i32x4 lo = gld<i32x4>(p), hi = gld<i32x4>(p + 64);
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
@@ -53,25 +77,17 @@ __device__ __forceinline__ f32x4 mma_f8f4(i32x8 a, i32x4 b, f32x4 c, uint32_t ea
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, widen(b), c, 0, 4, 0, (int)ea, 0, (int)eb);
 }
 
-// Activation row of tile row r (clamped into the group) for the gate/up phase.
-__device__ __forceinline__ void act_row(const GArgs& A, const GroupInfo& gi, int r, const uint8_t*& base,
-                                        const uint8_t*& ebase, long& ar) {
-    if (gi.shared) {
-        ar = r;
-        base = A.a_sh;
-        ebase = (const uint8_t*)A.a_sh_scale;
-    } else {
-        const int pp = gi.p0 + r;
-        ar = A.src ? A.src[pp] / A.src_div : pp;
-        base = A.a;
-        ebase = (const uint8_t*)A.a_scale;
-    }
+// Row of the activation matrix that tile row r (< gi.m) reads in the gate/up phase.
+__device__ __forceinline__ long act_row(const GArgs& A, const GroupInfo& gi, int r) {
+    if (gi.shared) return r;
+    const int pp = gi.p0 + r;
+    return A.src ? A.src[pp] / A.src_div : pp;
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- gate / up
-template <int MB, int KS, int P>
+template <int MB, int KS, int P, int kNB>
 __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     constexpr int NW = 4 / KS;                 // waves along N
     constexpr int TN = NW * kNB * 16;          // h columns per tile (a multiple of 32)
@@ -98,15 +114,15 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
         const Bank bk = gi.shared ? A.shared : A.routed;
         const int k0 = kw * nsteps * 128;
 
+        const uint8_t* abase = gi.shared ? A.a_sh : A.a;
+        const uint8_t* aebase = (const uint8_t*)(gi.shared ? A.a_sh_scale : A.a_scale);
         const uint8_t* ap[MB];
         const uint8_t* aep[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const uint8_t *base, *ebase;
-            long ar;
-            act_row(A, gi, min(m0 + i * 16 + lane % 16, gi.m - 1), base, ebase, ar);
-            ap[i] = base + (size_t)ar * H + k0 + kq * 16;
-            aep[i] = ebase + (size_t)ar * (H / 32) + k0 / 32;
+            const long ar = act_row(A, gi, min(m0 + i * 16 + lane % 16, gi.m - 1));
+            ap[i] = abase + (size_t)ar * H + k0 + kq * 16;
+            aep[i] = aebase + (size_t)ar * (H / 32) + k0 / 32;
         }
         const uint8_t *gp[kNB], *up[kNB], *gep[kNB], *uep[kNB];
 #pragma unroll
@@ -131,15 +147,15 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
         auto load = [&](int p, int step) {
 #pragma unroll
             for (int c = 0; c < kNB; ++c) {
-                rg[p][c] = *(const i32x4*)(gp[c] + step * 64);
-                ru[p][c] = *(const i32x4*)(up[c] + step * 64);
-                rge[p][c] = *(const uint32_t*)(gep[c] + step * 4);
-                rue[p][c] = *(const uint32_t*)(uep[c] + step * 4);
+                rg[p][c] = gld<i32x4>(gp[c] + step * 64);
+                ru[p][c] = gld<i32x4>(up[c] + step * 64);
+                rge[p][c] = gld<uint32_t>(gep[c] + step * 4);
+                rue[p][c] = gld<uint32_t>(uep[c] + step * 4);
             }
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 ra[p][i] = load_act(ap[i] + step * 128);
-                rae[p][i] = *(const uint32_t*)(aep[i] + step * 4);
+                rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
             }
         };
         auto mma = [&](int p) {
@@ -157,12 +173,17 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
         const int nmain = nsteps / P * P;
         if (nmain > 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) load(p, p);
+            for (int p = 0; p < P; ++p) {
+                load(p, p);
+                pin();
+            }
             for (int s0 = 0; s0 < nmain - P; s0 += P) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     mma(p);
+                    pin();
                     load(p, s0 + P + p);
+                    pin();
                 }
             }
 #pragma unroll
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
 }
 
 // ---------------------------------------------------------------- down
-template <int MB, int P>
+template <int MB, int P, int kNB>
 __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
     constexpr int TN = 4 * kNB * 16;           // output (H) columns per tile; each wave all of K
     constexpr int RS = TN + 1;
@@ -277,13 +298,13 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
         auto load = [&](int p, int step) {
 #pragma unroll
             for (int c = 0; c < kNB; ++c) {
-                rd[p][c] = *(const i32x4*)(dp[c] + step * 64);
-                rde[p][c] = *(const uint32_t*)(dep[c] + step * 4);
+                rd[p][c] = gld<i32x4>(dp[c] + step * 64);
+                rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
             }
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 ra[p][i] = load_act(ap[i] + step * 128);
-                rae[p][i] = *(const uint32_t*)(aep[i] + step * 4);
+                rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
             }
         };
         auto mma = [&](int p) {
@@ -296,12 +317,17 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
         const int nmain = nsteps / P * P;
         if (nmain > 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) load(p, p);
+            for (int p = 0; p < P; ++p) {
+                load(p, p);
+                pin();
+            }
             for (int s0 = 0; s0 < nmain - P; s0 += P) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     mma(p);
+                    pin();
                     load(p, s0 + P + p);
+                    pin();
                 }
             }
 #pragma unroll
@@ -351,19 +377,45 @@ static int mx_persistent_grid(K kernel) {
 // The K split of gate/up over two waves needs an even number of 128-wide
 // k-steps (H % 256 == 0); otherwise every wave covers all of K.  Tiles of 16
 // rows keep 4 k-steps of loads in flight, tiles of 64 rows 2 (registers).
+#ifndef MOE_MX_GU_KS
+#define MOE_MX_GU_KS 1
+#endif
+#ifndef MOE_MX_GU_P
+#define MOE_MX_GU_P 8
+#endif
+#ifndef MOE_MX_GU_NB
+#define MOE_MX_GU_NB 2
+#endif
+#ifndef MOE_MX_DN_P
+#define MOE_MX_DN_P 4
+#endif
+#ifndef MOE_MX_DN_NB
+#define MOE_MX_DN_NB 4
+#endif
+// 16-row tiles: K split over MOE_MX_GU_KS waves when the 128-wide k-steps
+// divide evenly, MOE_MX_GU_NB column blocks per wave when I is a multiple of
+// the tile width (else 2); 64-row tiles: two k-steps in flight (registers).
 hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
-    const bool split = (A.H / 128) % 2 == 0;
+    const int nst = A.H / 128;
+    constexpr int KS = MOE_MX_GU_KS, NB = MOE_MX_GU_NB;
+    static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     if (mb == 1) {
-        if (split) MOE_MX_LAUNCH((mx_gateup_kernel<1, 2, 4>)); else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, 4>));
+        if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, MOE_MX_GU_P, NB>));
+        else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, MOE_MX_GU_P, 2>));
     } else {
-        if (split) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2>)); else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2>));
+        if (nst % 2 == 0) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2, 2>)); else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2, 2>));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
-    if (mb == 1) MOE_MX_LAUNCH((mx_down_kernel<1, 4>));
-    else MOE_MX_LAUNCH((mx_down_kernel<4, 2>));
+    constexpr int NB = MOE_MX_DN_NB;
+    if (mb == 1) {
+        if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, NB>));
+        else MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, 2>));
+    } else {
+        MOE_MX_LAUNCH((mx_down_kernel<4, 2, 2>));
+    }
     return hipGetLastError();
 }
 #undef MOE_MX_LAUNCH

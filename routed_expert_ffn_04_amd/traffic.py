@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 from routed_expert_ffn_04_amd.accounting import sources_digest  # noqa: E402
 
 PROBE = os.path.join(HERE, "moe_probe")
-GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::gffn_build_lists")
+GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::gffn_build_lists")
 NAMES = {
     1: "tiny-fp32-T64-H256-E8-top2",
     2: "dsv3-decode-bf16-T128-H7168-E256+1-top8",
@@ -40,6 +40,8 @@ NAMES = {
     4: "ep-prefill-share-fp8-9+1groups-H7168-I2048",
     5: "dsv3-prefill-fp8-T16384-H7168-E256+1-top8",
 }
+MXFP4_NAMES = {2: "dsv3-decode-mxfp4-T128-H7168-E256+1-top8", 3: "dsv3-skew-mxfp4-T4096-H7168-E256+1-top8-zipf1.2",
+               5: "dsv3-prefill-mxfp4-T16384-H7168-E256+1-top8"}
 
 
 def run(cmd, log):
@@ -74,9 +76,11 @@ def pmc_pass(counter, probe_args, work, tag):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--configs", type=int, nargs="+", default=[2, 5])
+    ap.add_argument("--configs", type=int, nargs="*", default=[2, 5])
     ap.add_argument("--fp8-combine-configs", type=int, nargs="*", default=[],
                     help="fp8 layer workloads to measure also with the FP8 combine")
+    ap.add_argument("--mxfp4-configs", type=int, nargs="*", default=[],
+                    help="layer workloads to measure also with MXFP4 expert weights")
     ap.add_argument("--calls", type=int, default=2, help="timed calls per probe run (one more is the warm-up)")
     ap.add_argument("--work", default="/tmp/moe_traffic", help="scratch (dumped inputs, raw counter files)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
@@ -95,12 +99,15 @@ def main():
         print(f"calibration {counter}: {kib:.0f} KiB per 1 GiB copy -> {gib / kib:.1f} bytes per KiB", flush=True)
 
     result = {"sources_sha256": sources_digest(), "calibration": cal, "workloads": {}}
-    runs = [(c, False) for c in args.configs] + [(c, True) for c in args.fp8_combine_configs]
-    for cid, fp8c in runs:
-        tag = f"c{cid}" + ("f" if fp8c else "")
+    runs = ([(c, "") for c in args.configs] + [(c, "fp8c") for c in args.fp8_combine_configs]
+            + [(c, "mxfp4") for c in args.mxfp4_configs])
+    for cid, var in runs:
+        fp8c = var == "fp8c"
+        tag = f"c{cid}" + {"": "", "fp8c": "f", "mxfp4": "m"}[var]
+        flag = {"": [], "fp8c": ["--fp8-combine"], "mxfp4": ["--mxfp4"]}[var]
         d = os.path.join(args.work, f"inputs_{tag}")
-        run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(cid), "--dump-inputs", d]
-            + (["--fp8-combine"] if fp8c else []), os.path.join(args.work, f"dump_{tag}.log"))
+        run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(cid), "--dump-inputs", d] + flag,
+            os.path.join(args.work, f"dump_{tag}.log"))
         ncalls = args.calls + 1
         rec = {"calls": ncalls, "kernels": {}}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -117,10 +124,13 @@ def main():
         rec["command"] = (f"python -m routed_expert_ffn_04_amd.traffic --configs {' '.join(map(str, args.configs))}"
                           + (f" --fp8-combine-configs {' '.join(map(str, args.fp8_combine_configs))}"
                              if args.fp8_combine_configs else "")
+                          + (f" --mxfp4-configs {' '.join(map(str, args.mxfp4_configs))}"
+                             if args.mxfp4_configs else "")
                           + f" (probe: moe_probe file <dump of bench.py --config {cid}"
-                          + (" --fp8-combine" if fp8c else "") + f"> {args.calls})")
-        result["workloads"][NAMES[cid] + ("+fp8-combine" if fp8c else "")] = rec
-        print(f"config {cid}{' fp8 combine' if fp8c else ''}: grouped FFN per call: fetch {rec['fetch_bytes'] / 1e9:.3f} GB, "
+                          + "".join(" " + f for f in flag) + f"> {args.calls})")
+        name = MXFP4_NAMES[cid] if var == "mxfp4" else NAMES[cid] + ("+fp8-combine" if fp8c else "")
+        result["workloads"][name] = rec
+        print(f"config {cid} {var}: grouped FFN per call: fetch {rec['fetch_bytes'] / 1e9:.3f} GB, "
               f"write {rec['write_bytes'] / 1e9:.3f} GB", flush=True)
     os.makedirs(os.path.dirname(args.out), exist_ok=True)
     with open(args.out, "w") as f:

@@ -38,6 +38,9 @@ def test_dump_inputs_layout(tmp_path):
     r = synth.routing_inputs(1)
     assert os.path.getsize(tmp_path / "x.bin") == r["x"].numel() * 4
     assert os.path.getsize(tmp_path / "w_router.bin") == r["w_router"].numel() * 4
+    bench.dump_inputs(2, str(tmp_path / "m"), mxfp4=True)
+    meta = dict(line.split(" ", 1) for line in open(tmp_path / "m" / "meta.txt").read().splitlines())
+    assert meta["w_dt"] == "mxfp4" and meta["x_dt"] == "bf16" and meta["T"] == "128"
     bench.dump_inputs(4, str(tmp_path / "g"))
     meta = dict(line.split(" ", 1) for line in open(tmp_path / "g" / "meta.txt").read().splitlines())
     assert meta["kind"] == "grouped" and len(meta["groups"].split()) == 9

@@ -45,11 +45,13 @@ def _sample(T, n, seed):
     return sorted(set([0, T - 1] + rng.choice(T, size=n, replace=False).tolist()))
 
 
-@pytest.mark.parametrize("cid,nsample,fp8c", [(1, None, False), (2, 6, False), (3, 6, False), (5, 4, False),
-                                              (5, 3, True)])
-def test_layer_config_full_size(cid, nsample, fp8c):
-    print(f"config {cid}{' with the fp8 combine' if fp8c else ''}: generating", flush=True)
-    wl = synth.config(cid, device=DEV)
+@pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 6, False, False),
+                                                    (3, 6, False, False), (5, 4, False, False), (5, 3, True, False),
+                                                    (2, 6, False, True)])
+def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
+    print(f"config {cid}{' with the fp8 combine' if fp8c else ''}{' with MXFP4 weights' if mxfp4 else ''}: generating",
+          flush=True)
+    wl = synth.config_mxfp4(cid, device=DEV) if mxfp4 else synth.config(cid, device=DEV)
     wl.y_dt = "e4m3" if fp8c else None
     run = bench.LayerRunner(wl, DEV, fp8_combine=fp8c)
     for _, f in run.calls():
@@ -67,7 +69,7 @@ def test_layer_config_full_size(cid, nsample, fp8c):
     np.testing.assert_array_equal(run.src.cpu().numpy(), src)
     np.testing.assert_array_equal(run.dest.cpu().numpy(), dest)
     out = run.out.float().cpu().numpy()
-    fp8 = wl.w_dt == "e4m3"
+    fp8 = wl.w_dt in ("e4m3", "mxfp4")
     if nsample is None:
         ref = om.moe_layer(wl)
         _check(out, ref["out"], fp8, f"config {cid} all tokens")

@@ -58,6 +58,7 @@ GROUPED_CASES = [
     ([130, 5, 0, 64, 1], 40, 256, 256),        # 16-row and 64-row tiles, a ragged 130
     ([3, 77, 200], 0, 384, 512),               # odd number of 128-wide k-steps (no K split)
     ([16, 17, 2], 33, 512, 384),               # class boundaries; odd k-steps in the down projection
+    ([9, 40, 3], 20, 1280, 1152),              # full rings of loads in flight plus tails, both projections
 ]
 
 
