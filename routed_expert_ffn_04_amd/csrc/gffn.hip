@@ -30,6 +30,11 @@ struct ClassSpec {
     // with the large tiles, which read every row once per 128/256 columns.
     // 0: never.
     int promote_min;
+    // Class 1 moves into class 0 (16-row tiles, weight tiles shared through
+    // L2 by the m-tiles of a group) when it has 1 .. demote_max members: a
+    // handful of groups (the shared expert at decode) would otherwise run
+    // alone in a launch that fills a fraction of the chip.  0: never.
+    int demote_max;
 };
 
 struct ListsOut {
@@ -103,15 +108,18 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         if (c >= 0) atomicAdd(&members[c], 1);
     }
     __syncthreads();
-    if (cs.promote_min > 0 && members[1] >= cs.promote_min) {
+    const int m1 = members[1];
+    const int to = (cs.demote_max > 0 && m1 > 0 && m1 <= cs.demote_max) ? 0
+                 : (cs.promote_min > 0 && m1 >= cs.promote_min)        ? 2 : 1;
+    if (to != 1) {
         for (int g = tid; g < ng; g += 1024)
             if (cls_of[g] == 1) {
-                cls_of[g] = 2;
-                mc_of[g].y = 2;
+                cls_of[g] = to;
+                mc_of[g].y = to;
             }
         __syncthreads();
         if (tid == 0) {
-            members[2] += members[1];
+            members[to] += m1;
             members[1] = 0;
         }
         __syncthreads();
@@ -170,6 +178,10 @@ static bool use_big(int dt, int H, int I, int R_max, int S) {
 }
 
 constexpr int kPromoteMin = 32;
+#ifndef MOE_DEMOTE_MAX
+#define MOE_DEMOTE_MAX 4
+#endif
+constexpr int kDemoteMax = MOE_DEMOTE_MAX;
 
 // MXFP4: groups of up to this many rows take the 16-row streaming tiles
 // (several m-tiles of one group re-read its weights, mostly from L2).
@@ -185,11 +197,13 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
         c.mlo[0] = 0;  c.mhi[0] = kMxC0Max; c.bm[0] = 16;
         c.mlo[1] = kMxC0Max; c.mhi[1] = 1 << 30;  c.bm[1] = 64;
         c.mlo[2] = 0;  c.mhi[2] = 0;        c.bm[2] = 64;   // unused
+        c.demote_max = kDemoteMax;
     } else if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
         c.promote_min = bm2 == 256 ? kPromoteMin : 0;
+        c.demote_max = kDemoteMax;
     } else {
         c.mlo[0] = 0;  c.mhi[0] = 0;        c.bm[0] = 16;   // unused
         c.mlo[1] = 0;  c.mhi[1] = 0;        c.bm[1] = 64;   // unused

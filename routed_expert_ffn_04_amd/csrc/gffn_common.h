@@ -112,6 +112,23 @@ struct TileIter {
     __device__ void next() { t += stride; }
 };
 
+// Tile t of a list -> (entry, n-tile).  Entry-major order keeps the n-tiles
+// of one m-tile together (one die's L2 serves their shared activation rows);
+// n-major order keeps the m-tiles of one weight tile together, so a group cut
+// into several 16-row m-tiles reads each weight tile from HBM once and from
+// L2 for the other m-tiles.
+#ifndef MOE_NMAJOR
+#define MOE_NMAJOR 1
+#endif
+template <bool NMAJOR>
+__device__ __forceinline__ int2 tile_coords(const TileList& L, long t, int ntn) {
+    if (NMAJOR && MOE_NMAJOR) {
+        const int c = *L.count;
+        return make_int2((int)(t % c), (int)(t / c));
+    }
+    return make_int2((int)(t / ntn), (int)(t % ntn));
+}
+
 // Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);

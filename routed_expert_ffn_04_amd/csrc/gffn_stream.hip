@@ -59,10 +59,11 @@ __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L)
     for (TileIter it(L, ntn); it.valid(); it.next()) {
         const int t = (int)it.t;
         __syncthreads();   // the previous tile's reduction is done with `red`
-        const int2 tl = L.entries[t / ntn];
+        const int2 tc = tile_coords<MB == 1>(L, t, ntn);
+        const int2 tl = L.entries[tc.x];
         const GroupInfo gi = group_info(A, tl.x);
         const int m0 = tl.y;
-        const int nt0 = (t % ntn) * TN;
+        const int nt0 = tc.y * TN;
         const int n0 = nt0 + nw * kNB * 16;
         const Bank& bk = gi.shared ? A.shared : A.routed;
         const int kb = kw * nsteps * 32 + (lane / 16) * 8;
@@ -180,10 +181,11 @@ __global__ __launch_bounds__(256) void stream_down_kernel(GArgs A, TileList L) {
     for (TileIter it(L, ntn); it.valid(); it.next()) {
         const int t = (int)it.t;
         __syncthreads();   // the previous tile's reduction is done with `red`
-        const int2 tl = L.entries[t / ntn];
+        const int2 tc = tile_coords<MB == 1>(L, t, ntn);
+        const int2 tl = L.entries[tc.x];
         const GroupInfo gi = group_info(A, tl.x);
         const int m0 = tl.y;
-        const int nt0 = (t % ntn) * TN;
+        const int nt0 = tc.y * TN;
         const int n0 = nt0 + nw * kNB * 16;
         const Bank& bk = gi.shared ? A.shared : A.routed;
         const int kb = kw * nsteps * 32 + (lane / 16) * 8;
