@@ -70,11 +70,10 @@ def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False, mxfp4: bool =
     log(f"config {cid} inputs written to {out_dir}")
 
 
-def measured_traffic(name: str):
-    """HBM bytes per grouped-FFN call from the stored counter runs
-    (profiles/traffic.json, written by routed_expert_ffn_04_amd.traffic),
-    or None when there is no record for this workload or the kernel sources
-    changed since it was taken."""
+def measured_record(name: str):
+    """The stored counter record of a workload (profiles/traffic.json,
+    written by routed_expert_ffn_04_amd.traffic), or None when there is none
+    or the kernel sources changed since it was taken."""
     path = os.path.join(HERE, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -83,7 +82,12 @@ def measured_traffic(name: str):
         return None
     if rec.get("sources_sha256") != accounting.sources_digest():
         return None
-    w = rec.get("workloads", {}).get(name)
+    return rec.get("workloads", {}).get(name)
+
+
+def measured_traffic(name: str):
+    """HBM bytes per grouped-FFN call from the stored counter runs, or None."""
+    w = measured_record(name)
     return None if w is None else int(w["bytes"])
 
 
@@ -171,29 +175,81 @@ class GroupedRunner:
             shared=self.shared, y=self.y, y_sh=self.y_sh, ws=self.ws)
 
 
+class ClockSampler:
+    """The GPU's shader clock while the timed steps run: a host thread reads
+    the current DPM level of the visible card (sysfs pp_dpm_sclk, the line
+    marked '*') every few milliseconds.  None where the file is absent."""
+
+    def __init__(self, period_s: float = 0.005):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if len(paths) == 1 else None   # one visible card, else ambiguous
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split()[0].lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return {"source": self.path, "samples": len(s), "min_mhz": s[0], "median_mhz": s[len(s) // 2],
+                "max_mhz": s[-1]}
+
+
 def run_timed(runner, steps: int, warmup: int):
     for _ in range(warmup):
         for _, f in runner.calls():
             f()
     torch.cuda.synchronize()
     evs = []
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        row = []
-        for name, f in runner.calls():
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            f()
-            e1.record()
-            row.append((name, e0, e1))
-        evs.append(row)
-    end = torch.cuda.Event(enable_timing=True)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        start = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            row = []
+            for name, f in runner.calls():
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                f()
+                e1.record()
+                row.append((name, e0, e1))
+            evs.append(row)
+        end = torch.cuda.Event(enable_timing=True)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    runner.clock = clk.summary()
     total_ms = start.elapsed_time(end)
     per = {}
     for row in evs:
@@ -251,8 +307,14 @@ def cpu_baseline(wl, cid: int, sample_tokens: int):
             sample = f"first {sample_tokens} of {wl.T} tokens (each token routed and run through its experts)"
         dt = time.perf_counter() - t0
     unit = "rows/s" if cid == 4 else "tokens/s"
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(n / dt, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": model}
 
 
 def main():
@@ -320,7 +382,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_TFLOPS[wl.w_dt], "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_TFLOPS[wl.w_dt], 4), "traffic": None}
-    roof["traffic"] = measured_traffic(wl.name + ("+fp8-combine" if args.fp8_combine else ""))
+    rec = measured_record(wl.name + ("+fp8-combine" if args.fp8_combine else ""))
+    roof["traffic"] = None if rec is None else int(rec["bytes"])
+    # matrix-core busy fraction of the same kernels (SQ_VALU_MFMA_BUSY_CYCLES), from the counter runs
+    roof["mfma_busy"] = None if rec is None else rec.get("mfma_busy_frac")
     roof["kernel"] = "moe_grouped_ffn (tile list + gate/up + down kernels)"
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -347,6 +412,7 @@ def main():
         "roofline": roof,
         "grouped_ffn": {"ms": round(gffn_ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)},
         "calls_ms": {k: round(v, 4) for k, v in per.items()},
+        "gpu_clock": getattr(runner, "clock", None),
     }
     if cid in (1, 4):
         # small working sets: also the call with caches scrubbed before each repetition

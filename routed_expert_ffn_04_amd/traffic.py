@@ -10,9 +10,15 @@ then runs the native probe (no torch) on exactly that routing under two
 rocprofv3 counter passes, FETCH_SIZE and WRITE_SIZE, and sums the counters of
 the grouped-FFN kernels per call.  The counters are scaled by what they read
 for a plain device copy of 1 GiB (probe mode "copy"), so the figures are
-bytes.  The result goes to profiles/traffic.json together with a digest of
-the kernel sources; bench.py reports the figure only while the sources still
-match that digest.
+bytes.  A third pass reads SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: the
+fraction of SIMD cycles the matrix cores were busy during the grouped-FFN
+kernels is busy / (active / XCDS x CUs x 4 SIMDs), GRBM_GUI_ACTIVE being
+summed over the accelerator dies (each has its own graphics register bus
+manager).  At T = 16384 this gives about 0.31 for 1.31 PFLOP/s, i.e. about
+4.2 PFLOP/s at full occupancy of the matrix cores, the rate that
+register-only MFMA loops reach on this chip.  The result goes to
+profiles/traffic.json together with a digest of the kernel sources; bench.py
+reports the figures only while the sources still match that digest.
 """
 from __future__ import annotations
 
@@ -33,6 +39,7 @@ from routed_expert_ffn_04_amd.accounting import sources_digest  # noqa: E402
 
 PROBE = os.path.join(HERE, "moe_probe")
 GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::gffn_build_lists")
+XCDS = 8          # MI355X accelerator dies
 NAMES = {
     1: "tiny-fp32-T64-H256-E8-top2",
     2: "dsv3-decode-bf16-T128-H7168-E256+1-top8",
@@ -53,25 +60,31 @@ def run(cmd, log):
         raise RuntimeError(f"{' '.join(cmd)} failed ({r.returncode}):\n{tail}")
 
 
-def counter_sums(out_dir):
-    """{kernel name: [per-dispatch counter values]} of one pass."""
+def counter_sums(out_dir, by_counter=False):
+    """{kernel name: [per-dispatch counter values]} of one pass (summed over
+    counters), or {kernel name: {counter: [per-dispatch values]}}."""
     files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise RuntimeError(f"no counter file under {out_dir}")
     per = {}
     for fn in files:
         for r in csv.DictReader(open(fn)):
-            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
-            per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: list(v.values()) for k, v in per.items()}
+            key = r["Counter_Name"] if by_counter else ""
+            d = per.setdefault(r["Kernel_Name"], {}).setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if by_counter:
+        return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+    return {k: list(cs[""].values()) for k, cs in per.items()}
 
 
-def pmc_pass(counter, probe_args, work, tag):
-    out = os.path.join(work, f"{tag}_{counter}")
+def pmc_pass(counters, probe_args, work, tag):
+    """One rocprofv3 counter pass (space-separated counters of one pass)."""
+    out = os.path.join(work, f"{tag}_{counters.split()[0]}")
     shutil.rmtree(out, ignore_errors=True)
-    cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--", PROBE, *probe_args]
+    cmd = ["rocprofv3", "--pmc", *counters.split(), "--output-format", "csv", "-d", out, "-o", "run", "--", PROBE,
+           *probe_args]
     run(["timeout", "-s", "KILL", "120", *cmd], out + ".log")
-    return counter_sums(out)
+    return counter_sums(out, by_counter=len(counters.split()) > 1)
 
 
 def main():
@@ -98,7 +111,9 @@ def main():
         cal[counter] = {"kib_per_gib_copy": kib, "bytes_per_kib": gib / kib}
         print(f"calibration {counter}: {kib:.0f} KiB per 1 GiB copy -> {gib / kib:.1f} bytes per KiB", flush=True)
 
-    result = {"sources_sha256": sources_digest(), "calibration": cal, "workloads": {}}
+    cus = int(subprocess.run([sys.executable, "-c", "import torch; print(torch.cuda.get_device_properties(0).multi_processor_count)"],
+                             capture_output=True, text=True, timeout=300).stdout.strip().splitlines()[-1])
+    result = {"sources_sha256": sources_digest(), "calibration": cal, "compute_units": cus, "workloads": {}}
     runs = ([(c, "") for c in args.configs] + [(c, "fp8c") for c in args.fp8_combine_configs]
             + [(c, "mxfp4") for c in args.mxfp4_configs])
     for cid, var in runs:
@@ -121,6 +136,15 @@ def main():
                 tot += b
             rec[counter.lower().replace("_size", "_bytes")] = round(tot)
         rec["bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+        per = pmc_pass("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE", ["file", d, str(args.calls)], args.work, tag + "_mfma")
+        busy = active = 0.0
+        for k, vals in per.items():
+            if any(s in k for s in GFFN_KERNELS):
+                busy += sum(vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+                active += sum(vals["GRBM_GUI_ACTIVE"])
+        rec["mfma_busy_cycles"] = round(busy / ncalls)
+        rec["grbm_gui_active"] = round(active / ncalls)
+        rec["mfma_busy_frac"] = round(busy / (active / XCDS * cus * 4), 4) if active else None
         rec["command"] = (f"python -m routed_expert_ffn_04_amd.traffic --configs {' '.join(map(str, args.configs))}"
                           + (f" --fp8-combine-configs {' '.join(map(str, args.fp8_combine_configs))}"
                              if args.fp8_combine_configs else "")
