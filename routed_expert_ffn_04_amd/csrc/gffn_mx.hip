@@ -37,19 +37,6 @@ namespace moe {
 namespace {
 
 
-// Scheduling barriers that keep each step's refill loads right behind that
-// step's MFMAs.  Off: measured on MI355X, the compiler's own order (refills
-// gathered at the end of the ring, waits counted per step) streams ~40%
-// faster.
-#ifndef MOE_MX_PIN
-#define MOE_MX_PIN 0
-#endif
-__device__ __forceinline__ void pin() {
-#if MOE_MX_PIN
-    __builtin_amdgcn_sched_barrier(0);
-#endif
-}
-
 __device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
 
 // Loads through global-address-space pointers: every operand lives in device
@@ -170,21 +157,19 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                 }
         };
         // ring of P k-steps in flight over the largest multiple of P, then
-        // the remaining steps one at a time
+        // the remaining steps one at a time.  The compiler gathers the refill
+        // loads at the end of each ring and counts its waits per step;
+        // scheduling barriers that pin each refill behind its step's MFMAs
+        // were measured ~40% slower.
         const int nmain = nsteps / P * P;
         if (nmain > 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                load(p, p);
-                pin();
-            }
+            for (int p = 0; p < P; ++p) load(p, p);
             for (int s0 = 0; s0 < nmain - P; s0 += P) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     mma(p);
-                    pin();
                     load(p, s0 + P + p);
-                    pin();
                 }
             }
 #pragma unroll
@@ -319,17 +304,12 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
         const int nmain = nsteps / P * P;
         if (nmain > 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                load(p, p);
-                pin();
-            }
+            for (int p = 0; p < P; ++p) load(p, p);
             for (int s0 = 0; s0 < nmain - P; s0 += P) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     mma(p);
-                    pin();
                     load(p, s0 + P + p);
-                    pin();
                 }
             }
 #pragma unroll
