@@ -58,6 +58,17 @@ __device__ __forceinline__ i32x8 load_act(const uint8_t* p) {
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// Exponents in 16-step blocks: a lane of lane group g loads the 16 bytes of
+// its row's exponents for steps 4g .. 4g+3 of the block (one dword per step,
+// one byte per K block of the step), and at step s of the block a lane takes
+// dword s % 4 of lane group s / 4 of its row by a cross-lane read
+// (ds_bpermute), then shifts out its own byte.  One 16-byte load per stream
+// and 16 steps instead of a dword per step: the exponent loads had cost the
+// streaming kernels 10-15% of their time.
+__device__ __forceinline__ uint32_t xlane(int src_lane, int v) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+
 // D += A(fp8, exponents ea) x B(fp4, exponents eb); the low byte of ea / eb
 // is this lane's E8M0 (operand formats: 0 = FP8 E4M3, 4 = FP4 E2M1).
 __device__ __forceinline__ f32x4 mma_f8f4(i32x8 a, i32x4 b, f32x4 c, uint32_t ea, uint32_t eb) {
@@ -74,7 +85,7 @@ __device__ __forceinline__ long act_row(const GArgs& A, const GroupInfo& gi, int
 }  // namespace
 
 // ---------------------------------------------------------------- gate / up
-template <int MB, int KS, int P, int kNB>
+template <int MB, int KS, int P, int kNB, bool XEX>
 __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     constexpr int NW = 4 / KS;                 // waves along N
     constexpr int TN = NW * kNB * 16;          // h columns per tile (a multiple of 32)
@@ -89,6 +100,7 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     const int kw = wave % KS, nw = wave / KS;
     const int kq = lane / 16;                  // K block of this lane within a step
     const uint32_t esh = 8u * kq;              // its exponent byte within the step's dword
+    constexpr bool XE = XEX && P % 4 == 0 && 16 % P == 0;   // exponents in 16-step blocks
 
     for (TileIter it(L, ntn); it.valid(); it.next()) {
         const int t = (int)it.t;
@@ -132,52 +144,110 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
         uint32_t rae[P][MB];
         i32x4 rg[P][kNB], ru[P][kNB];
         uint32_t rge[P][kNB], rue[P][kNB];
-        auto load = [&](int p, int step) {
+        // exponent blocks (XE): current and next 16 steps
+        i32x4 xcg[kNB], xcu[kNB], xca[MB], xng[kNB], xnu[kNB], xna[MB];
+        auto load_w = [&](int p, int step) {
 #pragma unroll
             for (int c = 0; c < kNB; ++c) {
                 rg[p][c] = gld<i32x4>(gp[c] + step * 64);
                 ru[p][c] = gld<i32x4>(up[c] + step * 64);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i) ra[p][i] = load_act(ap[i] + step * 128);
+        };
+        auto load_e = [&](int p, int step) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
                 rge[p][c] = gld<uint32_t>(gep[c] + step * 4);
                 rue[p][c] = gld<uint32_t>(uep[c] + step * 4);
             }
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                ra[p][i] = load_act(ap[i] + step * 128);
-                rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
-            }
+            for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
         };
-        auto mma = [&](int p) {
+        auto load_x = [&](int blk, i32x4 (&xg)[kNB], i32x4 (&xu)[kNB], i32x4 (&xa)[MB]) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                xg[c] = gld<i32x4>(gep[c] + blk * 64 + kq * 16);
+                xu[c] = gld<i32x4>(uep[c] + blk * 64 + kq * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i) xa[i] = gld<i32x4>(aep[i] + blk * 64 + kq * 16);
+        };
+        auto next_block = [&]() {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                xcg[c] = xng[c];
+                xcu[c] = xnu[c];
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i) xca[i] = xna[i];
+        };
+        // step p of the ring; s0 (a multiple of 4 when XE) is the ring's first step
+        auto mma = [&](int p, int s0, bool x) {
+            uint32_t ea[MB], eg[kNB], eu[kNB];
+            if (x) {
+                const int src = (lane & 15) + 16 * (((s0 + p) & 15) >> 2);
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) {
+                    eg[c] = xlane(src, xcg[c][p & 3]) >> esh;
+                    eu[c] = xlane(src, xcu[c][p & 3]) >> esh;
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
+            } else {
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) {
+                    eg[c] = rge[p][c] >> esh;
+                    eu[c] = rue[p][c] >> esh;
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
+            }
 #pragma unroll
             for (int c = 0; c < kNB; ++c)
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    const uint32_t ea = rae[p][i] >> esh;
-                    accg[i][c] = mma_f8f4(ra[p][i], rg[p][c], accg[i][c], ea, rge[p][c] >> esh);
-                    accu[i][c] = mma_f8f4(ra[p][i], ru[p][c], accu[i][c], ea, rue[p][c] >> esh);
+                    accg[i][c] = mma_f8f4(ra[p][i], rg[p][c], accg[i][c], ea[i], eg[c]);
+                    accu[i][c] = mma_f8f4(ra[p][i], ru[p][c], accu[i][c], ea[i], eu[c]);
                 }
         };
-        // ring of P k-steps in flight over the largest multiple of P, then
-        // the remaining steps one at a time.  The compiler gathers the refill
-        // loads at the end of each ring and counts its waits per step;
-        // scheduling barriers that pin each refill behind its step's MFMAs
-        // were measured ~40% slower.
-        const int nmain = nsteps / P * P;
+        // ring of P k-steps in flight over the largest multiple of P (of 16
+        // with XE), then the remaining steps one at a time.  The compiler
+        // gathers the refill loads at the end of each ring and counts its
+        // waits per step; scheduling barriers that pin each refill behind its
+        // step's MFMAs were measured ~40% slower.
+        const int nmain = XE ? nsteps / 16 * 16 : nsteps / P * P;
         if (nmain > 0) {
-#pragma unroll
-            for (int p = 0; p < P; ++p) load(p, p);
-            for (int s0 = 0; s0 < nmain - P; s0 += P) {
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    mma(p);
-                    load(p, s0 + P + p);
-                }
+            if (XE) {
+                load_x(0, xcg, xcu, xca);
+                if (nmain > 16) load_x(1, xng, xnu, xna);
             }
 #pragma unroll
-            for (int p = 0; p < P; ++p) mma(p);
+            for (int p = 0; p < P; ++p) {
+                load_w(p, p);
+                if (!XE) load_e(p, p);
+            }
+            int s0 = 0;
+            for (; s0 < nmain - P; s0 += P) {
+                if (XE && s0 > 0 && (s0 & 15) == 0) {
+                    next_block();
+                    if (s0 + 16 < nmain) load_x(s0 / 16 + 1, xng, xnu, xna);
+                }
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    mma(p, s0, XE);
+                    load_w(p, s0 + P + p);
+                    if (!XE) load_e(p, s0 + P + p);
+                }
+            }
+            if (XE && s0 > 0 && (s0 & 15) == 0) next_block();
+#pragma unroll
+            for (int p = 0; p < P; ++p) mma(p, s0, XE);
         }
         for (int s = nmain; s < nsteps; ++s) {
-            load(0, s);
-            mma(0);
+            load_w(0, s);
+            load_e(0, s);
+            mma(0, s, false);
         }
 
         // partial sums -> LDS; row = i*16 + 4*(lane/16) + q, col = nw*32 + c*16 + lane%16
@@ -230,7 +300,7 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
 }
 
 // ---------------------------------------------------------------- down
-template <int MB, int P, int kNB>
+template <int MB, int P, int kNB, bool XEX>
 __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
     constexpr int TN = 4 * kNB * 16;           // output (H) columns per tile; each wave all of K
     constexpr int RS = TN + 1;
@@ -244,6 +314,7 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
     const int kq = lane / 16;
     const uint32_t esh = 8u * kq;
     const uint8_t* he = (const uint8_t*)A.h_scale;
+    constexpr bool XE = XEX && P % 4 == 0 && 16 % P == 0;   // exponents in 16-step blocks
 
     for (TileIter it(L, ntn); it.valid(); it.next()) {
         const int t = (int)it.t;
@@ -282,42 +353,82 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
         uint32_t rae[P][MB];
         i32x4 rd[P][kNB];
         uint32_t rde[P][kNB];
-        auto load = [&](int p, int step) {
+        i32x4 xcd[kNB], xca[MB], xnd[kNB], xna[MB];   // exponent blocks (XE): current, next
+        auto load_w = [&](int p, int step) {
 #pragma unroll
-            for (int c = 0; c < kNB; ++c) {
-                rd[p][c] = gld<i32x4>(dp[c] + step * 64);
-                rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
-            }
+            for (int c = 0; c < kNB; ++c) rd[p][c] = gld<i32x4>(dp[c] + step * 64);
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                ra[p][i] = load_act(ap[i] + step * 128);
-                rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
-            }
+            for (int i = 0; i < MB; ++i) ra[p][i] = load_act(ap[i] + step * 128);
         };
-        auto mma = [&](int p) {
+        auto load_e = [&](int p, int step) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
+        };
+        auto load_x = [&](int blk, i32x4 (&xd)[kNB], i32x4 (&xa)[MB]) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) xd[c] = gld<i32x4>(dep[c] + blk * 64 + kq * 16);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) xa[i] = gld<i32x4>(aep[i] + blk * 64 + kq * 16);
+        };
+        auto next_block = [&]() {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) xcd[c] = xnd[c];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) xca[i] = xna[i];
+        };
+        auto mma = [&](int p, int s0, bool x) {
+            uint32_t ea[MB], ed[kNB];
+            if (x) {
+                const int src = (lane & 15) + 16 * (((s0 + p) & 15) >> 2);
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) ed[c] = xlane(src, xcd[c][p & 3]) >> esh;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
+            } else {
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) ed[c] = rde[p][c] >> esh;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
+            }
 #pragma unroll
             for (int c = 0; c < kNB; ++c)
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    acc[i][c] = mma_f8f4(ra[p][i], rd[p][c], acc[i][c], rae[p][i] >> esh, rde[p][c] >> esh);
+                for (int i = 0; i < MB; ++i) acc[i][c] = mma_f8f4(ra[p][i], rd[p][c], acc[i][c], ea[i], ed[c]);
         };
-        const int nmain = nsteps / P * P;
+        const int nmain = XE ? nsteps / 16 * 16 : nsteps / P * P;
         if (nmain > 0) {
-#pragma unroll
-            for (int p = 0; p < P; ++p) load(p, p);
-            for (int s0 = 0; s0 < nmain - P; s0 += P) {
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    mma(p);
-                    load(p, s0 + P + p);
-                }
+            if (XE) {
+                load_x(0, xcd, xca);
+                if (nmain > 16) load_x(1, xnd, xna);
             }
 #pragma unroll
-            for (int p = 0; p < P; ++p) mma(p);
+            for (int p = 0; p < P; ++p) {
+                load_w(p, p);
+                if (!XE) load_e(p, p);
+            }
+            int s0 = 0;
+            for (; s0 < nmain - P; s0 += P) {
+                if (XE && s0 > 0 && (s0 & 15) == 0) {
+                    next_block();
+                    if (s0 + 16 < nmain) load_x(s0 / 16 + 1, xnd, xna);
+                }
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    mma(p, s0, XE);
+                    load_w(p, s0 + P + p);
+                    if (!XE) load_e(p, s0 + P + p);
+                }
+            }
+            if (XE && s0 > 0 && (s0 & 15) == 0) next_block();
+#pragma unroll
+            for (int p = 0; p < P; ++p) mma(p, s0, XE);
         }
         for (int s = nmain; s < nsteps; ++s) {
-            load(0, s);
-            mma(0);
+            load_w(0, s);
+            load_e(0, s);
+            mma(0, s, false);
         }
 
 #pragma unroll
@@ -368,35 +479,48 @@ static int mx_persistent_grid(K kernel) {
 #ifndef MOE_MX_GU_NB
 #define MOE_MX_GU_NB 2
 #endif
+#ifndef MOE_MX_GU_XE
+#define MOE_MX_GU_XE 0
+#endif
 #ifndef MOE_MX_DN_P
 #define MOE_MX_DN_P 4
 #endif
 #ifndef MOE_MX_DN_NB
 #define MOE_MX_DN_NB 4
 #endif
-// 16-row tiles: K split over MOE_MX_GU_KS waves when the 128-wide k-steps
-// divide evenly, MOE_MX_GU_NB column blocks per wave when I is a multiple of
-// the tile width (else 2); 64-row tiles: two k-steps in flight (registers).
+#ifndef MOE_MX_DN_XE
+#define MOE_MX_DN_XE 1
+#endif
+// 16-row tiles.  gate/up: K split over MOE_MX_GU_KS waves when the 128-wide
+// k-steps divide evenly, MOE_MX_GU_NB column blocks per wave when I is a
+// multiple of the tile width (else 2), 8 k-steps in flight with an exponent
+// dword per step (the 16-step exponent blocks need registers that a ring of
+// 8 leaves no room for, and a ring of 4 with them measured 1% slower).
+// down: 4 k-steps in flight with 16-step exponent blocks (5% faster than
+// per-step exponents).  64-row tiles: two k-steps in flight (registers).
 hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     const int nst = A.H / 128;
     constexpr int KS = MOE_MX_GU_KS, NB = MOE_MX_GU_NB;
+    constexpr bool XE = MOE_MX_GU_XE;
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     if (mb == 1) {
-        if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, MOE_MX_GU_P, NB>));
-        else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, MOE_MX_GU_P, 2>));
+        if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, MOE_MX_GU_P, NB, XE>));
+        else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, MOE_MX_GU_P, 2, XE>));
     } else {
-        if (nst % 2 == 0) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2, 2>)); else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2, 2>));
+        if (nst % 2 == 0) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2, 2, false>));
+        else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2, 2, false>));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     constexpr int NB = MOE_MX_DN_NB;
+    constexpr bool XE = MOE_MX_DN_XE;
     if (mb == 1) {
-        if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, NB>));
-        else MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, 2>));
+        if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, NB, XE>));
+        else MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, 2, XE>));
     } else {
-        MOE_MX_LAUNCH((mx_down_kernel<4, 2, 2>));
+        MOE_MX_LAUNCH((mx_down_kernel<4, 2, 2, false>));
     }
     return hipGetLastError();
 }

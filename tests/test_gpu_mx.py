@@ -59,6 +59,7 @@ GROUPED_CASES = [
     ([3, 77, 200], 0, 384, 512),               # odd number of 128-wide k-steps (no K split)
     ([16, 17, 2], 33, 512, 384),               # class boundaries; odd k-steps in the down projection
     ([9, 40, 3], 20, 1280, 1152),              # full rings of loads in flight plus tails, both projections
+    ([5, 30, 2], 18, 4352, 2176),              # exponents in 16-step blocks (2 blocks + 2 / 1 block + 1 tail steps)
     # more than a handful of 17..256-row groups: they keep the 64-row tiles
     # (up to four such groups are cut into 16-row tiles instead)
     ([20, 33, 50, 70, 100, 5, 250], 17, 512, 256),
