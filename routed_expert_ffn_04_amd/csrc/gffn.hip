@@ -10,7 +10,9 @@
 //   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
 //                             or 64-row LDS tiles (fp32 or H % 256 != 0)
 // (fp32 and e4m3 layers put every group in class 2; MXFP4 layers use the
-// MX weight-streaming tiles of gffn_mx.hip: 16 rows for m <= 16, else 64).  One single-workgroup kernel
+// MX weight-streaming tiles of gffn_mx.hip, 16 rows for m <= 16 and 64 up to
+// 256, and the 256 x 256 MX tiles of gffn_mxbig.hip above, with the same
+// promotion of many mid-sized groups as bf16).  One single-workgroup kernel
 // writes, per class, the list of (group, first row) m-tiles with the heaviest
 // groups first (longest-processing-time order); then each class's gate/up
 // kernel and down kernel run as persistent grids that walk their list (see
@@ -177,6 +179,14 @@ static bool use_big(int dt, int H, int I, int R_max, int S) {
            (uint64_t)H * I * eb < lim;
 }
 
+// Large MXFP4 tiles (gffn_mxbig.hip): 256-column down tiles, 32-bit byte
+// offsets of activation / h rows and of a weight matrix.
+static bool use_mxbig(int H, int I, int R_max, int S) {
+    const uint64_t lim = (uint64_t)1 << 32;
+    return H % 256 == 0 && (uint64_t)std::max(R_max, S) * H < lim && ((uint64_t)R_max + S) * I < lim &&
+           (uint64_t)H * I / 2 < lim;
+}
+
 constexpr int kPromoteMin = 32;
 #ifndef MOE_DEMOTE_MAX
 #define MOE_DEMOTE_MAX 4
@@ -194,10 +204,12 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
     const int bm2 = use_big(dt, H, I, R_max, S) ? 256 : 64;
     if (dt == DT_MXFP4) {
+        const bool big = use_mxbig(H, I, R_max, S);
         c.mlo[0] = 0;  c.mhi[0] = kMxC0Max; c.bm[0] = 16;
-        c.mlo[1] = kMxC0Max; c.mhi[1] = 1 << 30;  c.bm[1] = 64;
-        c.mlo[2] = 0;  c.mhi[2] = 0;        c.bm[2] = 64;   // unused
+        c.mlo[1] = kMxC0Max; c.mhi[1] = big ? 256 : 1 << 30;  c.bm[1] = 64;
+        c.mlo[2] = 256; c.mhi[2] = big ? 1 << 30 : 0;  c.bm[2] = 256;
         c.demote_max = kDemoteMax;
+        c.promote_min = big ? kPromoteMin : 0;
     } else if (dt == DT_BF16) {
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
@@ -276,13 +288,13 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     // phase 1 (all classes), then phase 2: a group's down tiles need all of its h
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = p.dt == DT_MXFP4 ? launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s)
+        e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_gateup(A, up[k], s) : launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s))
           : k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
                   : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
-        e = p.dt == DT_MXFP4 ? launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s)
+        e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_down(A, dn[k], s) : launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s))
           : k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
                   : cs.bm[k] == 256 ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
     }

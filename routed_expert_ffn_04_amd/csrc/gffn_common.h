@@ -129,7 +129,8 @@ __device__ __forceinline__ int2 tile_coords(const TileList& L, long t, int ntn) 
     return make_int2((int)(t / ntn), (int)(t % ntn));
 }
 
-// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip).
+// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip,
+// gffn_mxbig.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
@@ -138,6 +139,8 @@ hipError_t launch_big_gateup(int dt, const GArgs& A, const TileList& L, hipStrea
 hipError_t launch_big_down(int dt, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mxbig_gateup(const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mxbig_down(const GArgs& A, const TileList& L, hipStream_t s);
 int device_cu_count();
 
 }  // namespace moe

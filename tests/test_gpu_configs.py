@@ -47,7 +47,7 @@ def _sample(T, n, seed):
 
 @pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 6, False, False),
                                                     (3, 6, False, False), (5, 4, False, False), (5, 3, True, False),
-                                                    (2, 6, False, True)])
+                                                    (2, 6, False, True), (5, 3, False, True)])
 def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
     print(f"config {cid}{' with the fp8 combine' if fp8c else ''}{' with MXFP4 weights' if mxfp4 else ''}: generating",
           flush=True)

@@ -63,6 +63,12 @@ GROUPED_CASES = [
     # more than a handful of 17..256-row groups: they keep the 64-row tiles
     # (up to four such groups are cut into 16-row tiles instead)
     ([20, 33, 50, 70, 100, 5, 250], 17, 512, 256),
+    # 256 x 256 MX tiles: exact, partial (one row over) and multi m-tiles, a large shared group
+    ([300, 600, 257, 20, 512], 280, 512, 256),
+    # a 16-stage K ring (three stages rotating) in gate/up, partial tiles
+    ([700, 260], 0, 2048, 384),
+    # 36 groups of 17..116 rows: promoted to the 256-row MX tiles
+    ([17 + (g * 37) % 100 for g in range(36)], 50, 512, 256),
 ]
 
 
