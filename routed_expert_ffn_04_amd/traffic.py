@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 from routed_expert_ffn_04_amd.accounting import sources_digest  # noqa: E402
 
 PROBE = os.path.join(HERE, "moe_probe")
-GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::gffn_build_lists")
+GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::mxbig_kernel", "moe::gffn_build_lists")
 XCDS = 8          # MI355X accelerator dies
 NAMES = {
     1: "tiny-fp32-T64-H256-E8-top2",
