@@ -158,6 +158,10 @@ GROUPED_CASES = [
     # m-tile boundaries of the 256-row tiles: exact multiples, one short, one over
     ([256, 512, 255, 257, 1], 256, 512, 256, "e4m3"),
     ([256, 512, 255, 257, 1], 0, 512, 256, "bf16"),
+    # partial m-tiles ending inside and at the edge of 8-row load groups and of
+    # the first and second 64-row load waves
+    ([265, 282, 320, 329, 263], 0, 512, 256, "e4m3"),
+    ([265, 282, 320, 329, 263], 0, 512, 256, "bf16"),
 ]
 
 
