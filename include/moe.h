@@ -122,6 +122,7 @@ size_t moe_route_workspace_size(int32_t T, int32_t E);
 moe_status_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                          int32_t* counts, int32_t* offsets, int32_t* src, int32_t* dest,
                          void* ws, size_t ws_bytes, void* stream);
+/* 0 for invalid sizes, including T * k > 2^30. */
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
 
 /* ---- activation quantisation (the BF16 -> FP8 cast of section 2.3.1) ------
@@ -167,7 +168,9 @@ moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t 
  * (from the fp32 accumulators) with the scales in y_scale [R_max][H/128]
  * (E4M3 y needs E4M3 weights and H a multiple of 256; y_scale is ignored
  * otherwise).  y_sh: [S][H] of type y_sh_dt (F32 or BF16).
- * routed->n must equal G; H, I multiples of 128. */
+ * routed->n must equal G; H, I multiples of 128.  A call with rows to
+ * process needs G >= 1 (the shared expert alone, G = 0, returns
+ * MOE_ERR_UNSUPPORTED) and a non-NULL offsets array. */
 moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale,
                              const int32_t* src, int32_t src_div,
                              const int32_t* offsets, int32_t G, int32_t R_max,

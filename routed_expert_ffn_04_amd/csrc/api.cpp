@@ -110,7 +110,7 @@ moe_status_t moe_route(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
 
 // ------------------------------------------------------------------ permute
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
-    if (T < 0 || k <= 0 || E <= 0) return 0;
+    if (T < 0 || k <= 0 || E <= 0 || (long long)T * k > (1LL << 30)) return 0;
     return al(moe::permute_ws_bytes(T * k, E));
 }
 
@@ -195,12 +195,10 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale, c
         return fail(MOE_ERR_INVALID, "grouped_ffn: MXFP8 exponents must be 4-byte aligned");
     if ((a && !aligned16(a)) || (a_sh && !aligned16(a_sh))) return fail(MOE_ERR_INVALID, "grouped_ffn: misaligned a");
     if ((R_max == 0 || G == 0) && !has_sh) return MOE_OK;
+    if (G == 0) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: the shared expert alone (G = 0) is not supported");
+    if (!offsets) return fail(MOE_ERR_INVALID, "grouped_ffn: null offsets");
     if (!ws || ws_bytes < moe_grouped_ffn_workspace_size(R_max, G, has_sh ? S : 0, H, I, wdt))
         return fail(MOE_ERR_WORKSPACE, "grouped_ffn: workspace");
-    if (G == 0 || !offsets) {
-        // shared expert only: a one-entry offsets array lives at the end of ws? keep it simple:
-        return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: G = 0 is not supported");
-    }
     moe::GffnProblem p{};
     p.dt = wdt; p.a = a; p.a_scale = (const float*)a_scale; p.src = src; p.src_div = src ? src_div : 1;
     p.offsets = offsets; p.G = G; p.R_max = R_max;

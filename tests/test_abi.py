@@ -39,6 +39,7 @@ def test_workspace_queries_are_host_only():
     L = moe.lib()
     assert L.moe_route_workspace_size(128, 256) >= 128 * 256 * 4
     assert L.moe_permute_workspace_size(16384, 8, 256) > 0
+    assert L.moe_permute_workspace_size(1 << 28, 8, 256) == 0      # T * k beyond 2^30
     a = L.moe_layer_workspace_size(128, 7168, 256, 8, 2048, 1, 1, 1, 0, 0)
     b = L.moe_layer_workspace_size(16384, 7168, 256, 8, 2048, 1, 2, 1, 1, 1)
     assert b > a > 128 * 8 * 7168 * 4
@@ -123,6 +124,12 @@ def test_grouped_ffn_validation():
     assert call(moe.MXFP8, mx4, a_s=P + 2) == moe.MOE_ERR_INVALID            # exponents 4-byte aligned
     assert call(moe.MXFP8, mx4, a_s=P, y_dt=2) == moe.MOE_ERR_UNSUPPORTED    # no e4m3 outputs from MXFP4
     assert call(moe.MXFP8, mx4, a_s=P, ws=16) == moe.MOE_ERR_WORKSPACE       # valid up to the workspace
+    # the shared expert alone (G = 0) is refused; so is a routed call without offsets
+    sh = _bank(1, 256, 256, moe.BF16)
+    assert L.moe_grouped_ffn(P, moe.BF16, None, None, 1, None, 0, 0, None, P, None, 16, ctypes.byref(sh),
+                             P, 0, None, P, 0, P, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_ffn(P, moe.BF16, None, P, 2, None, 8, 0, ctypes.byref(b), P, None, 16, ctypes.byref(sh),
+                             P, 0, None, P, 0, P, 1 << 40, None) == moe.MOE_ERR_INVALID
 
 
 def test_layer_validation():
