@@ -65,6 +65,8 @@ ROUTE_CASES = [
     (5, 128, 16, 16, "softmax", "f32", False),        # k = E
     (9, 128, 1024, 3, "sigmoid", "bf16", False),      # E at the maximum
     (11, 128, 7, 1, "softmax", "f32", False),         # k = 1
+    (20, 1536, 24, 4, "sigmoid", "bf16", True),       # 512-long h chunks, ragged T and E
+    (3, 768, 12, 2, "softmax", "f32", False),         # 256-long h chunks, fp32 x
 ]
 
 
