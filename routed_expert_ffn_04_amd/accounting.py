@@ -64,10 +64,18 @@ def grouped_ffn_bytes(group_rows, shared_rows: int, H: int, I: int, a_dt: str, w
     return b
 
 
+# Sources that build or launch the grouped-FFN kernels (the kernels whose
+# traffic is recorded): the kernel files and their headers, the C ABI that
+# carves the workspace and fills the launch arguments, and its header.  The
+# router, permute, quantisation and combine kernels are not among them.
+def _gffn_source(name: str) -> bool:
+    return name.startswith("gffn") or name in ("common.h", "internal.h", "api.cpp", "moe.h")
+
+
 def sources_digest() -> str:
-    """sha256 over the library's kernel and ABI sources (csrc/, include/),
-    in name order: the key that ties a stored traffic measurement to the
-    kernels it was taken on."""
+    """sha256 over the sources of the grouped-FFN kernels and the C ABI
+    (csrc/, include/; see _gffn_source), in name order: the key that ties a
+    stored traffic measurement to the kernels it was taken on."""
     import hashlib
     import os
     here = os.path.dirname(os.path.abspath(__file__))
@@ -76,7 +84,7 @@ def sources_digest() -> str:
     for d in (os.path.join(here, "csrc"), os.path.join(root, "include")):
         for name in sorted(os.listdir(d)):
             path = os.path.join(d, name)
-            if os.path.isfile(path):
+            if os.path.isfile(path) and _gffn_source(name):
                 h.update(name.encode())
                 with open(path, "rb") as f:
                     h.update(f.read())

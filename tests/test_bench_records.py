@@ -62,3 +62,12 @@ def test_traffic_lookup_requires_matching_sources(tmp_path, monkeypatch):
 def test_sources_digest_is_stable():
     assert accounting.sources_digest() == accounting.sources_digest()
     assert len(accounting.sources_digest()) == 64
+
+
+def test_sources_digest_covers_grouped_ffn_only():
+    # the digest keys the grouped-FFN traffic record: it covers the grouped-FFN
+    # kernels and the C ABI, not the router / permute / quant / combine kernels
+    assert accounting._gffn_source("gffn_big.hip") and accounting._gffn_source("gffn_common.h")
+    assert accounting._gffn_source("api.cpp") and accounting._gffn_source("moe.h")
+    for other in ("route.hip", "permute.hip", "quant.hip", "combine.hip", "moe_probe.cpp"):
+        assert not accounting._gffn_source(other)
