@@ -339,7 +339,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        print("bench.py: the library has no multi-GPU path, so only --gpus 1 is measured", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
