@@ -264,9 +264,13 @@ static int persistent_grid(K kernel) {
     return per_cu * device_cu_count();
 }
 
-// K is split over the 4 waves when every wave still gets a multiple of kP
-// k-steps of 32; otherwise each wave covers all of K (K is a multiple of 128,
-// so K/32 is a multiple of 4; kP must divide it).
+// Tiles of 16 rows: each wave streams whole weight rows (all of K) for its 32
+// h columns.  Measured on the T = 128 decode batch, this is about 1% faster
+// per layer than splitting K over the four waves, which reads every weight
+// row in four pieces.  Tiles of 64 rows split K over the 4 waves when every
+// wave still gets a multiple of kP k-steps of 32; otherwise each wave covers
+// all of K (K is a multiple of 128, so K/32 is a multiple of 4; kP must
+// divide it).
 #define MOE_STREAM_LAUNCH(KERNEL, MBV, KSV)                                              \
     do {                                                                                 \
         static const int g = persistent_grid(KERNEL<MBV, KSV>);                          \
@@ -275,11 +279,9 @@ static int persistent_grid(K kernel) {
 
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     const bool split = MOE_STREAM_KS_GATEUP == 4 && A.H % (32 * 4 * kP) == 0;
-    if (mb == 1) {
-        if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 4); else MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1);
-    } else {
-        if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 4); else MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 1);
-    }
+    if (mb == 1) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1);
+    else if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 4);
+    else MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 1);
     return hipGetLastError();
 }
 
