@@ -205,10 +205,12 @@ def test_grouped_ffn_parity(gm, sm, H, I, dt, y_dt):
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("y_dt,out_dt,shared", [("f32", "f32", True), ("bf16", "bf16", True), ("f32", "bf16", False),
-                                               ("e4m3", "bf16", True), ("e4m3", "f32", False)])
-def test_combine_parity(y_dt, out_dt, shared):
-    T, k, H = 50, 4, 384
+@pytest.mark.parametrize("y_dt,out_dt,shared,k", [("f32", "f32", True, 4), ("bf16", "bf16", True, 4), ("f32", "bf16", False, 4),
+                                                 ("e4m3", "bf16", True, 4), ("e4m3", "f32", False, 4),
+                                                 # expert rows in chunks of 8: one full chunk plus a remainder, two plus one
+                                                 ("f32", "f32", True, 12), ("bf16", "bf16", False, 9), ("e4m3", "bf16", True, 17)])
+def test_combine_parity(y_dt, out_dt, shared, k):
+    T, H = 50, 384
     rng = np.random.default_rng(1)
     R = T * k
     dest = rng.permutation(R).astype(np.int32)
