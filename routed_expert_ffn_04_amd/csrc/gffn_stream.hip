@@ -28,14 +28,22 @@ namespace moe {
 #endif
 constexpr int kP = MOE_STREAM_P;      // k-steps of loads in flight per wave
 #ifndef MOE_STREAM_PG
-#define MOE_STREAM_PG 8
+#define MOE_STREAM_PG 16
+#endif
+#ifndef MOE_STREAM_NBG
+#define MOE_STREAM_NBG 1
 #endif
 #ifndef MOE_STREAM_PD
 #define MOE_STREAM_PD 8
 #endif
 constexpr int kPD = MOE_STREAM_PD;    // the same for the 16-row down tiles (8: 0.5% faster than 4 at T = 128)
-constexpr int kPG = MOE_STREAM_PG;    // the same for the 16-row gate/up tiles (whole K per wave; 8 measured
-                                      // 0.7% faster than 4 on the T = 128 decode layer, 2 slower)
+// 16-row gate/up tiles (whole K per wave): k-steps in flight and 16-column
+// blocks per wave.  On the T = 128 decode layer, one block with 16 k-steps in
+// flight (two 1 KiB weight fragments per k-step and wave, two workgroups per
+// CU) beat two blocks with 8 (4.06 -> 3.87 ms of grouped FFN), which beat two
+// with 4 (4.08 ms) and 2 (4.15 ms).  H not a multiple of 512: 4 in flight.
+constexpr int kPG = MOE_STREAM_PG;
+constexpr int kNBG = MOE_STREAM_NBG;
 constexpr int kNB = 2;                // 16-column blocks per wave
 
 // Weight loads use the default cache policy: measured on MI355X, the
@@ -51,10 +59,10 @@ __device__ __forceinline__ bf16x8 ldw(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 lda(const uint16_t* p) { return *(const bf16x8*)p; }
 
 // ---------------------------------------------------------------- gate / up
-template <int MB, int KS, int P>
+template <int MB, int KS, int P, int NB>
 __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L) {
     constexpr int NW = 4 / KS;                 // waves along N
-    constexpr int TN = NW * kNB * 16;          // h columns per tile
+    constexpr int TN = NW * NB * 16;          // h columns per tile
     constexpr int RS = 2 * TN + 1;             // LDS row stride (floats)
     const int H = A.H, I = A.I;
     const int ntn = I / TN;
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L)
         const GroupInfo gi = group_info(A, tl.x);
         const int m0 = tl.y;
         const int nt0 = tc.y * TN;
-        const int n0 = nt0 + nw * kNB * 16;
+        const int n0 = nt0 + nw * NB * 16;
         const Bank& bk = gi.shared ? A.shared : A.routed;
         const int kb = kw * nsteps * 32 + (lane / 16) * 8;
 
@@ -95,27 +103,27 @@ __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L)
             }
             ap[i] = base + (size_t)ar * H + kb;
         }
-        const uint16_t* gp[kNB];
-        const uint16_t* up[kNB];
+        const uint16_t* gp[NB];
+        const uint16_t* up[NB];
 #pragma unroll
-        for (int c = 0; c < kNB; ++c) {
+        for (int c = 0; c < NB; ++c) {
             const size_t row = (size_t)gi.e * I + n0 + c * 16 + lane % 16;
             gp[c] = (const uint16_t*)bk.wg + row * H + kb;
             up[c] = (const uint16_t*)bk.wu + row * H + kb;
         }
 
-        f32x4 accg[MB][kNB], accu[MB][kNB];
+        f32x4 accg[MB][NB], accu[MB][NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int c = 0; c < kNB; ++c) accg[i][c] = accu[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < NB; ++c) accg[i][c] = accu[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // ring of P k-steps in flight; nsteps is a multiple of P, the body
         // is straight-line so the loads of later steps stay outstanding
-        bf16x8 ra[P][MB], rg[P][kNB], ru[P][kNB];
+        bf16x8 ra[P][MB], rg[P][NB], ru[P][NB];
         auto load = [&](int p, int step) {
 #pragma unroll
-            for (int c = 0; c < kNB; ++c) {
+            for (int c = 0; c < NB; ++c) {
                 rg[p][c] = ldw(gp[c] + step * 32);
                 ru[p][c] = ldw(up[c] + step * 32);
             }
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L)
         };
         auto mma = [&](int p) {
 #pragma unroll
-            for (int c = 0; c < kNB; ++c)
+            for (int c = 0; c < NB; ++c)
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
                     accg[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[p][i], rg[p][c], accg[i][c], 0, 0, 0);
@@ -147,11 +155,11 @@ __global__ __launch_bounds__(256) void stream_gateup_kernel(GArgs A, TileList L)
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int c = 0; c < kNB; ++c)
+            for (int c = 0; c < NB; ++c)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int row = i * 16 + 4 * (lane / 16) + q;
-                    const int col = nw * kNB * 16 + c * 16 + lane % 16;
+                    const int col = nw * NB * 16 + c * 16 + lane % 16;
                     red[kw][row][col] = accg[i][c][q];
                     red[kw][row][TN + col] = accu[i][c][q];
                 }
@@ -273,8 +281,8 @@ static int persistent_grid(K kernel) {
     return per_cu * device_cu_count();
 }
 
-// Tiles of 16 rows: each wave streams whole weight rows (all of K) for its 32
-// h columns.  Measured on the T = 128 decode batch, this is about 1% faster
+// Tiles of 16 rows: each wave streams whole weight rows (all of K) for its
+// kNBG * 16 h columns.  Measured on the T = 128 decode batch, this is about 1% faster
 // per layer than splitting K over the four waves, which reads every weight
 // row in four pieces.  Tiles of 64 rows split K over the 4 waves when every
 // wave still gets a multiple of kP k-steps of 32; otherwise each wave covers
@@ -288,10 +296,10 @@ static int persistent_grid(K kernel) {
 
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     const bool split = MOE_STREAM_KS_GATEUP == 4 && A.H % (32 * 4 * kP) == 0;
-    if (mb == 1 && A.H % (32 * kPG) == 0) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kPG);
-    else if (mb == 1) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kP);
-    else if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 4, kP);
-    else MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 1, kP);
+    if (mb == 1 && A.H % (32 * kPG) == 0) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kPG, kNBG);
+    else if (mb == 1) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kP, kNBG);
+    else if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 4, kP, kNB);
+    else MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 1, kP, kNB);
     return hipGetLastError();
 }
 
