@@ -45,9 +45,9 @@ def _sample(T, n, seed):
     return sorted(set([0, T - 1] + rng.choice(T, size=n, replace=False).tolist()))
 
 
-@pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 6, False, False),
+@pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 16, False, False),
                                                     (3, 6, False, False), (5, 4, False, False), (5, 3, True, False),
-                                                    (2, 6, False, True), (5, 3, False, True)])
+                                                    (2, 16, False, True), (5, 3, False, True)])
 def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
     print(f"config {cid}{' with the fp8 combine' if fp8c else ''}{' with MXFP4 weights' if mxfp4 else ''}: generating",
           flush=True)
