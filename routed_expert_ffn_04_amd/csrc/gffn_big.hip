@@ -189,7 +189,11 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
 
     for (int s = 0; s < nstages; ++s) {
         const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
-        __syncthreads();   // stage s and the scales of block s+1 landed; stage s-1 fully consumed
+        // this wave's direct loads of stage s and of block s+1's scales landed
+        // (the barrier alone does not wait for them), then every wave's;
+        // stage s-1 fully consumed
+        wait_vm<0>();
+        __syncthreads();
         if (s + 1 < nstages) {
             if (FP8 && tid < kBigM) {
                 // products of stage s+1 into buffer (s+1)&1, last read in stage s-1

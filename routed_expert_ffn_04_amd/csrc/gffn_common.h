@@ -129,6 +129,18 @@ __device__ __forceinline__ int2 tile_coords(const TileList& L, long t, int ntn) 
     return make_int2((int)(t / ntn), (int)(t % ntn));
 }
 
+// s_waitcnt with only the vector-memory count: vmcnt(n), expcnt and
+// lgkmcnt left at their maxima (gfx9 encoding: vmcnt[3:0] | expcnt << 4 |
+// lgkmcnt << 8 | vmcnt[5:4] << 14).  A workgroup barrier (__syncthreads) does
+// not wait for this wave's direct global->LDS loads on gfx950: its fence
+// orders LDS operations only, so a barrier that hands such data to other
+// waves needs wait_vm<0>() (or a count) before it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip,
 // gffn_mxbig.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);

@@ -57,15 +57,6 @@ __device__ __forceinline__ const uint8_t* wave_ptr(const void* p) {
     return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
-// s_waitcnt with only the vector-memory count: vmcnt(n), expcnt and
-// lgkmcnt left at their maxima (gfx9 encoding: vmcnt[3:0] | expcnt << 4 |
-// lgkmcnt << 8 | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 struct XSmem {
     uint8_t* stage;       // [3][48 KiB]
     uint32_t* ea;         // [3][256] token exponent dwords of a stage
