@@ -206,13 +206,17 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
             if (FP8 && s + 2 < nstages) issue_scales(S, ld, wsc0, wsc1, s + 2, wave, lane);
         }
         // The next stage's eight direct loads of this wave are spread over
-        // the first half of the compute: issued back to back they would stall
+        // the compute, two after each of blocks 1-4 (e4m3) or after each of
+        // the first two k-steps (bf16): issued back to back they would stall
         // the wave on a full load queue (the vector L1 keeps a bounded number
-        // of line misses in flight) before its first MFMA.
+        // of line misses in flight) before its first MFMA.  Measured for e4m3
+        // at T = 16384: after blocks 1-4 2-3% faster than after 0-3; after
+        // 2-5 the same as 0-3; after 3-6, four per block after 0-1, or one
+        // per block after 0-7, slower.
         const bool more = s + 1 < nstages;
         uint8_t* nbuf = S.stage_buf + ((s + 1) & 1) * kStageBytes;
         const int k1 = (s + 1) * kStage;
-        auto dma2 = [&](int b) {   // loads 2b and 2b+1, after compute block b < 4
+        auto dma2 = [&](int b) {   // loads 2b and 2b+1
             if (more) {
                 issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b);
                 issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b + 1);
@@ -259,7 +263,7 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                         for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], c, acc8[i][j][q]);
                     }
                 }
-                if (i < 4) dma2(i);
+                if (i >= 1 && i < 5) dma2(i - 1);
                 // keep the scheduler from hoisting later blocks' fragment reads
                 // (register pressure: the accumulators take half the budget)
                 __builtin_amdgcn_sched_barrier(0);
