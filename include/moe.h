@@ -93,7 +93,10 @@ typedef struct {
     const void* s_down;         /* E4M3: fp32 [n][H/128][I/128]; MXFP4: uint8 [n][H][I/32] */
 } moe_experts_t;
 
-/* ---- routing ------------------------------------------------------------
+/* ---- routing ("How DeepSeek inference works", "What does DeepSeek inference
+ * actually do per token?": a learned router scores the routed experts and keeps
+ * the top k, 8 of 256 in its worked example; "DeepSeek V3/R1 Inference
+ * Efficiency (2)", section 2.3.1, operator "Gate: router gate") -------------
  * For every token t and routed expert e the logit is one fp32 chain of fused
  * multiply-adds over h = 0..H-1 in ascending order,
  *     l[t][e] = fma-chain(x[t][h] * w_router[h][e]) + bias[e]   (+0 adds turn -0 into +0),
@@ -111,7 +114,9 @@ moe_status_t moe_route(const void* x, int32_t x_dt, int32_t T, int32_t H,
                        void* ws, size_t ws_bytes, void* stream);
 size_t moe_route_workspace_size(int32_t T, int32_t E);
 
-/* ---- permute ------------------------------------------------------------
+/* ---- permute ("DeepSeek V3/R1 Inference Efficiency (2)", section 2.3.1,
+ * operator "Expert: prepare routed GEMM": token-expert assignments gathered
+ * per expert before the grouped GEMM) ---------------------------------------
  * Groups the R = T*k assignments by expert (stable counting sort):
  *   counts[e]   number of assignments to expert e                 [E]
  *   offsets     exclusive prefix sum of counts, offsets[E] = R    [E+1]
@@ -146,7 +151,11 @@ moe_status_t moe_quant_e4m3_1x128(const void* x, int32_t x_dt, int32_t rows, int
 moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t cols,
                              uint8_t* q, uint8_t* e8m0, void* stream);
 
-/* ---- grouped FFN --------------------------------------------------------
+/* ---- grouped FFN ("DeepSeek V3/R1 Inference Efficiency (2)", section 2.3.1:
+ * routed "up & gate" [7168, 4096] and "down" [2048, 7168] grouped GEMMs with
+ * "Expert: SwiGLU" between them, and the shared expert GEMMs; section 2.4.1 for
+ * the decode sizes; section 1.b for efficiency against group count and rows
+ * per group) ----------------------------------------------------------------
  * For every routed group g (expert g of `routed`) and permuted row p in
  * [offsets[g], offsets[g+1]):
  *     a_p = a[src[p] / src_div]   (a[p] when src is NULL; src values in [0, R_max))
@@ -155,18 +164,22 @@ moe_status_t moe_quant_mxfp8(const void* x, int32_t x_dt, int32_t rows, int32_t 
  * and, when `shared` is non-NULL, the same with the shared expert for the S
  * rows of a_sh into y_sh.  h' is h at the precision the down projection
  * consumes: F32 weights -> fp32; BF16 -> rounded to bf16 (nearest even);
- * E4M3 -> quantised per row and 128-column block exactly as in
- * moe_quant_e4m3_1x128; MXFP4 -> MXFP8 per row and 32 columns exactly as in
- * moe_quant_mxfp8.  Accumulation is fp32.
+ * E4M3 -> quantised per row and 128-column block from its fp32 value by the
+ * rule of moe_quant_e4m3_1x128 (scale = amax / 448 and codes = h / scale, both
+ * IEEE fp32 divisions); MXFP4 -> MXFP8 per row and 32 columns by the rule of
+ * moe_quant_mxfp8.  The fp32 value of h itself depends on the accumulation
+ * order, so h's codes equal those of a reference only up to that rounding.
+ * Accumulation is fp32.
  * Supported (a_dt, weight dt): (F32, F32), (BF16, BF16), (E4M3, E4M3),
  * (MXFP8, MXFP4).  E4M3 activations carry fp32 a_scale [rows of a][H/128],
  * MXFP8 activations uint8 a_scale [rows of a][H/32] (a_sh_scale likewise).
  * offsets: [G+1] int32 device array with offsets[0] = 0 and
  * offsets[G] <= R_max (R_max, a host value, bounds the routed rows and sizes
  * the launch).  y: [R_max][H] of type y_dt: F32, BF16, or E4M3 = codes
- * quantised per row and 128-column block exactly as in moe_quant_e4m3_1x128
- * (from the fp32 accumulators) with the scales in y_scale [R_max][H/128]
- * (E4M3 y needs E4M3 weights and H a multiple of 256; y_scale is ignored
+ * quantised per row and 128-column block by the rule of moe_quant_e4m3_1x128
+ * from the fp32 accumulators, with the scales in y_scale [R_max][H/128]
+ * (E4M3 y needs E4M3 weights, H a multiple of 256, and max(R_max, S) * H and
+ * (R_max + S) * I below 2^32, else MOE_ERR_UNSUPPORTED; y_scale is ignored
  * otherwise).  y_sh: [S][H] of type y_sh_dt (F32 or BF16).
  * routed->n must equal G; H, I multiples of 128.  A call with rows to
  * process needs G >= 1 (the shared expert alone, G = 0, returns
@@ -194,13 +207,16 @@ moe_status_t moe_combine(const void* y_perm, int32_t y_dt, const float* y_scale,
                          const int32_t* dest, const float* topk_w, int32_t T, int32_t k,
                          int32_t H, void* out, int32_t out_dt, void* stream);
 
-/* ---- the whole layer ----------------------------------------------------
+/* ---- the whole layer (the MoE FFN of "How DeepSeek inference works" and of
+ * "DeepSeek V3/R1 Inference Efficiency (2)", section 2.3.1: gate, prepare
+ * routed GEMM, routed and shared expert GEMMs with SwiGLU, combine reduce) ---
  * route -> (E4M3 or MXFP4 weights: quantise x once per token, per 1x128
  * block or to MXFP8) -> permute -> grouped FFN over the routed groups and
  * the shared expert -> combine, all enqueued on `stream`.  Supported: x F32
  * with F32 weights; x BF16 with BF16, E4M3 or MXFP4 weights.  y_sh is kept in fp32 when out_dt is F32 and in bf16 when out_dt
  * is BF16; the routed expert outputs y_perm in y_dt: F32 or BF16, or E4M3
- * (the FP8 combine; E4M3 weights and H a multiple of 256 only).
+ * (the FP8 combine; E4M3 weights, H a multiple of 256, T*k*H and
+ * (T*k + T)*I below 2^32 only, else MOE_ERR_UNSUPPORTED).
  * topk_ids_out [T][k], topk_w_out [T][k], counts_out [E] are optional copies
  * of the routing results (NULL to skip). */
 moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H,

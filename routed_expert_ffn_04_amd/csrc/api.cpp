@@ -181,8 +181,11 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale, c
         return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: activation dtype %d with weights %d", a_dt, wdt);
     if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3)
         return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y dtype %d", y_dt);
-    if (y_dt == MOE_E4M3 && (wdt != MOE_E4M3 || H % 256))
-        return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: E4M3 y needs E4M3 weights and H %% 256 == 0 (H=%d)", H);
+    if (y_dt == MOE_E4M3 &&
+        (wdt != MOE_E4M3 || !moe::gffn_e4m3_y_supported(H, I, R_max, shared && S > 0 ? S : 0)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "grouped_ffn: E4M3 y needs E4M3 weights, H %% 256 == 0 and row offsets within 32 bits "
+                    "(H=%d I=%d R_max=%d S=%d)", H, I, R_max, S);
     if (y_sh_dt != MOE_F32 && y_sh_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "grouped_ffn: y_sh dtype %d", y_sh_dt);
     if (src && src_div <= 0) return fail(MOE_ERR_INVALID, "grouped_ffn: src_div=%d", src_div);
     const bool has_sh = shared && S > 0;
@@ -289,9 +292,12 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
     if (!ok_combo) return fail(MOE_ERR_UNSUPPORTED, "layer: x dtype %d with weights %d", x_dt, wdt);
     if (out_dt != MOE_F32 && out_dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "layer: out dtype %d", out_dt);
     if (y_dt != MOE_F32 && y_dt != MOE_BF16 && y_dt != MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "layer: y dtype %d", y_dt);
-    if (y_dt == MOE_E4M3 && (wdt != MOE_E4M3 || H % 256))
-        return fail(MOE_ERR_UNSUPPORTED, "layer: E4M3 y needs E4M3 weights and H %% 256 == 0 (H=%d)", H);
     if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "layer: T*k too large");
+    if (y_dt == MOE_E4M3 &&
+        (wdt != MOE_E4M3 || !moe::gffn_e4m3_y_supported(H, I, T * k, shared ? T : 0)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "layer: E4M3 y needs E4M3 weights, H %% 256 == 0 and row offsets within 32 bits "
+                    "(H=%d I=%d T*k=%lld)", H, I, (long long)T * k);
     if (T == 0) return MOE_OK;
     if (!out || !aligned16(out) || !aligned16(x)) return fail(MOE_ERR_INVALID, "layer: null or misaligned x/out");
     const int has_sh = shared ? 1 : 0;

@@ -155,15 +155,14 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
 }
 
 int device_cu_count() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cus[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
+    static DeviceCache cache;
+    return per_device(cache, [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    });
 }
 
 // ---------------------------------------------------------------- host side
@@ -179,6 +178,8 @@ static bool use_big(int dt, int H, int I, int R_max, int S) {
            (uint64_t)H * I * eb < lim;
 }
 
+bool gffn_e4m3_y_supported(int H, int I, int R_max, int S) { return use_big(DT_E4M3, H, I, R_max, S); }
+
 // Large MXFP4 tiles (gffn_mxbig.hip): 256-column down tiles, 32-bit byte
 // offsets of activation / h rows and of a weight matrix.
 static bool use_mxbig(int H, int I, int R_max, int S) {
@@ -188,17 +189,11 @@ static bool use_mxbig(int H, int I, int R_max, int S) {
 }
 
 constexpr int kPromoteMin = 32;
-#ifndef MOE_DEMOTE_MAX
-#define MOE_DEMOTE_MAX 4
-#endif
-constexpr int kDemoteMax = MOE_DEMOTE_MAX;
+constexpr int kDemoteMax = 4;
 
 // MXFP4: groups of up to this many rows take the 16-row streaming tiles
 // (several m-tiles of one group re-read its weights, mostly from L2).
-#ifndef MOE_MX_C0_MAX
-#define MOE_MX_C0_MAX 16
-#endif
-constexpr int kMxC0Max = MOE_MX_C0_MAX;
+constexpr int kMxC0Max = 16;
 
 static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};

@@ -330,14 +330,13 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                 const int hr = S.out_row[r];
                 if (hr < 0) continue;
                 const float amax = fmaxf(fmaxf(S.red[r], S.red[kBigM + r]), fmaxf(S.red[2 * kBigM + r], S.red[3 * kBigM + r]));
-                // scale amax / 448 (within an ulp); codes h * (448 / amax)
-                const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-                const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
+                // the activation rule: scale amax / 448, codes h / scale (IEEE divisions)
+                const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
                 if (wn == 0 && lane < 16) A.h_scale[(size_t)hr * (I / 128) + n0 / 128] = sc;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     *(uint32_t*)(A.h + (size_t)hr * I + n0 + wn * 32 + 16 * j + 4 * (lane / 16)) =
-                        f32x4_to_e4m3x4(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
+                        f32x4_to_e4m3x4(hv[i][j][0] / sc, hv[i][j][1] / sc, hv[i][j][2] / sc, hv[i][j][3] / sc);
             }
         } else {
 #pragma unroll
@@ -376,15 +375,14 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
                 const int yr = S.out_row[r];
                 if (yr < 0) continue;
                 const float amax = fmaxf(S.red[pw * kBigM + r], S.red[(pw + 1) * kBigM + r]);
-                // scale amax / 448 (within an ulp); codes y * (448 / amax)
-                const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-                const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
+                // the activation rule: scale amax / 448, codes y / scale (IEEE divisions)
+                const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
                 if ((wn & 1) == 0 && lane < 16) A.y_scale[(size_t)yr * (H / 128) + (n0 + wn * 64) / 128] = sc;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     *(uint32_t*)((uint8_t*)yb + (size_t)yr * H + n0 + wn * 64 + 16 * j + 4 * (lane / 16)) =
-                        f32x4_to_e4m3x4(acc8[i][j][0] * inv, acc8[i][j][1] * inv, acc8[i][j][2] * inv,
-                                        acc8[i][j][3] * inv);
+                        f32x4_to_e4m3x4(acc8[i][j][0] / sc, acc8[i][j][1] / sc, acc8[i][j][2] / sc,
+                                        acc8[i][j][3] / sc);
             }
         } else if (FP8) {
 #pragma unroll
@@ -535,10 +533,11 @@ constexpr size_t kBigLds = 2 * kStageBytes + kBigM * sizeof(uint32_t) + kBigM * 
 
 template <int DT, int PHASE>
 static hipError_t launch_big_t(const GArgs& A, const TileList& L, hipStream_t s) {
-    static const int grid = [] {
+    static DeviceCache cache;
+    const int grid = per_device(cache, [] {
         hipFuncSetAttribute((const void*)big_kernel<DT, PHASE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
         return device_cu_count();   // one 512-thread workgroup per CU (LDS-limited)
-    }();
+    });
     hipLaunchKernelGGL((big_kernel<DT, PHASE>), dim3(grid), dim3(512), kBigLds, s, A, L);
     return hipGetLastError();
 }

@@ -1,6 +1,8 @@
 // Shared definitions of the grouped expert FFN kernels: arguments, MFMA
 // operand traits, group lookup, and the persistent work queues.
 #pragma once
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -117,12 +119,9 @@ struct TileIter {
 // n-major order keeps the m-tiles of one weight tile together, so a group cut
 // into several 16-row m-tiles reads each weight tile from HBM once and from
 // L2 for the other m-tiles.
-#ifndef MOE_NMAJOR
-#define MOE_NMAJOR 1
-#endif
 template <bool NMAJOR>
 __device__ __forceinline__ int2 tile_coords(const TileList& L, long t, int ntn) {
-    if (NMAJOR && MOE_NMAJOR) {
+    if (NMAJOR) {
         const int c = *L.count;
         return make_int2((int)(t % c), (int)(t / c));
     }
@@ -154,5 +153,24 @@ hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t
 hipError_t launch_mxbig_gateup(const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_mxbig_down(const GArgs& A, const TileList& L, hipStream_t s);
 int device_cu_count();
+
+// Launch constants (persistent grid sizes) cached per device: computed on the
+// first launch on each device with that device current.  Concurrent first
+// calls compute the same value, so publishing it through a relaxed atomic is
+// race-free; devices beyond kMaxDevices recompute every time.
+constexpr int kMaxDevices = 64;
+using DeviceCache = std::atomic<int>[kMaxDevices];
+
+template <class F>
+int per_device(DeviceCache& cache, F compute) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return compute();
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = compute();
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
 
 }  // namespace moe

@@ -463,36 +463,24 @@ static int mx_persistent_grid(K kernel) {
 
 #define MOE_MX_LAUNCH(KERNEL)                                                       \
     do {                                                                            \
-        static const int g = mx_persistent_grid(KERNEL);                            \
+        static DeviceCache cache_;                                                  \
+        const int g = per_device(cache_, [] { return mx_persistent_grid(KERNEL); }); \
         hipLaunchKernelGGL(KERNEL, dim3(g), dim3(256), 0, s, A, L);                 \
     } while (0)
 
 // The K split of gate/up over two waves needs an even number of 128-wide
 // k-steps (H % 256 == 0); otherwise every wave covers all of K.  Tiles of 16
 // rows keep 4 k-steps of loads in flight, tiles of 64 rows 2 (registers).
-#ifndef MOE_MX_GU_KS
-#define MOE_MX_GU_KS 1
-#endif
-#ifndef MOE_MX_GU_P
-#define MOE_MX_GU_P 8
-#endif
-#ifndef MOE_MX_GU_NB
-#define MOE_MX_GU_NB 2
-#endif
-#ifndef MOE_MX_GU_XE
-#define MOE_MX_GU_XE 0
-#endif
-#ifndef MOE_MX_DN_P
-#define MOE_MX_DN_P 4
-#endif
-#ifndef MOE_MX_DN_NB
-#define MOE_MX_DN_NB 4
-#endif
-#ifndef MOE_MX_DN_XE
-#define MOE_MX_DN_XE 1
-#endif
-// 16-row tiles.  gate/up: K split over MOE_MX_GU_KS waves when the 128-wide
-// k-steps divide evenly, MOE_MX_GU_NB column blocks per wave when I is a
+// Tuning of the 16-row MX tiles (measured on the T = 128 decode layer):
+// gate/up covers all of K per wave (no split) with 8 k-steps in flight, two
+// 16-column blocks per wave and an exponent dword per step; down keeps 4
+// k-steps in flight over four 16-column blocks with 16-step exponent blocks.
+constexpr int kMxGuKs = 1, kMxGuP = 8, kMxGuNb = 2;
+constexpr bool kMxGuXe = false;
+constexpr int kMxDnP = 4, kMxDnNb = 4;
+constexpr bool kMxDnXe = true;
+// 16-row tiles.  gate/up: K split over kMxGuKs waves when the 128-wide
+// k-steps divide evenly, kMxGuNb column blocks per wave when I is a
 // multiple of the tile width (else 2), 8 k-steps in flight with an exponent
 // dword per step (the 16-step exponent blocks need registers that a ring of
 // 8 leaves no room for, and a ring of 4 with them measured 1% slower).
@@ -500,12 +488,12 @@ static int mx_persistent_grid(K kernel) {
 // per-step exponents).  64-row tiles: two k-steps in flight (registers).
 hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     const int nst = A.H / 128;
-    constexpr int KS = MOE_MX_GU_KS, NB = MOE_MX_GU_NB;
-    constexpr bool XE = MOE_MX_GU_XE;
+    constexpr int KS = kMxGuKs, NB = kMxGuNb;
+    constexpr bool XE = kMxGuXe;
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     if (mb == 1) {
-        if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, MOE_MX_GU_P, NB, XE>));
-        else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, MOE_MX_GU_P, 2, XE>));
+        if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, kMxGuP, NB, XE>));
+        else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, kMxGuP, 2, XE>));
     } else {
         if (nst % 2 == 0) MOE_MX_LAUNCH((mx_gateup_kernel<4, 2, 2, 2, false>));
         else MOE_MX_LAUNCH((mx_gateup_kernel<4, 1, 2, 2, false>));
@@ -514,11 +502,11 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
 }
 
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
-    constexpr int NB = MOE_MX_DN_NB;
-    constexpr bool XE = MOE_MX_DN_XE;
+    constexpr int NB = kMxDnNb;
+    constexpr bool XE = kMxDnXe;
     if (mb == 1) {
-        if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, NB, XE>));
-        else MOE_MX_LAUNCH((mx_down_kernel<1, MOE_MX_DN_P, 2, XE>));
+        if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, XE>));
+        else MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, 2, XE>));
     } else {
         MOE_MX_LAUNCH((mx_down_kernel<4, 2, 2, false>));
     }

@@ -189,7 +189,12 @@ __global__ __launch_bounds__(512) void mxbig_kernel(GArgs A, TileList L) {
             // this wave's loads of stage s done (stage s+1's may stay in flight), then everyone's
             if (s + 1 < nstages) wait_vm<kXDma>();
             else wait_vm<0>();
+            // compiler-only fences around the bare barrier (no waitcnt is
+            // emitted): LDS reads of stage s stay below it, writes of stage
+            // s-1 above it
+            asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
             // the buffer of stage s-1, which every wave has finished, takes stage s+2
             if (s + 2 < nstages) issue(s + 2);
 
@@ -279,10 +284,11 @@ __global__ __launch_bounds__(512) void mxbig_kernel(GArgs A, TileList L) {
 
 template <int PHASE>
 static hipError_t launch_mxbig_t(const GArgs& A, const TileList& L, hipStream_t s) {
-    static const int grid = [] {
+    static DeviceCache cache;
+    const int grid = per_device(cache, [] {
         hipFuncSetAttribute((const void*)mxbig_kernel<PHASE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLds);
         return device_cu_count();   // one 512-thread workgroup per CU (LDS-limited)
-    }();
+    });
     hipLaunchKernelGGL((mxbig_kernel<PHASE>), dim3(grid), dim3(512), kXLds, s, A, L);
     return hipGetLastError();
 }

@@ -17,44 +17,22 @@
 
 namespace moe {
 
-#ifndef MOE_STREAM_P
-#define MOE_STREAM_P 4
-#endif
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 0
-#endif
-#ifndef MOE_STREAM_KS_GATEUP
-#define MOE_STREAM_KS_GATEUP 4
-#endif
-constexpr int kP = MOE_STREAM_P;      // k-steps of loads in flight per wave
-#ifndef MOE_STREAM_PG
-#define MOE_STREAM_PG 16
-#endif
-#ifndef MOE_STREAM_NBG
-#define MOE_STREAM_NBG 1
-#endif
-#ifndef MOE_STREAM_PD
-#define MOE_STREAM_PD 8
-#endif
-constexpr int kPD = MOE_STREAM_PD;    // the same for the 16-row down tiles (8: 0.5% faster than 4 at T = 128)
+constexpr int kP = 4;                 // k-steps of loads in flight per wave (64-row tiles)
+constexpr int kPD = 8;                // the same for the 16-row down tiles (8: 0.5% faster than 4 at T = 128)
 // 16-row gate/up tiles (whole K per wave): k-steps in flight and 16-column
 // blocks per wave.  On the T = 128 decode layer, one block with 16 k-steps in
 // flight (two 1 KiB weight fragments per k-step and wave, two workgroups per
 // CU) beat two blocks with 8 (4.06 -> 3.87 ms of grouped FFN), which beat two
 // with 4 (4.08 ms) and 2 (4.15 ms).  H not a multiple of 512: 4 in flight.
-constexpr int kPG = MOE_STREAM_PG;
-constexpr int kNBG = MOE_STREAM_NBG;
+constexpr int kPG = 16;
+constexpr int kNBG = 1;
 constexpr int kNB = 2;                // 16-column blocks per wave
+// 64-row gate/up tiles split K over the four waves.
+constexpr int kKsGateup = 4;
 
 // Weight loads use the default cache policy: measured on MI355X, the
 // non-temporal hint made the streaming kernels ~15% slower.
-__device__ __forceinline__ bf16x8 ldw(const uint16_t* p) {
-#if MOE_STREAM_NT
-    return __builtin_nontemporal_load((const bf16x8*)p);
-#else
-    return *(const bf16x8*)p;
-#endif
-}
+__device__ __forceinline__ bf16x8 ldw(const uint16_t* p) { return *(const bf16x8*)p; }
 
 __device__ __forceinline__ bf16x8 lda(const uint16_t* p) { return *(const bf16x8*)p; }
 
@@ -290,12 +268,13 @@ static int persistent_grid(K kernel) {
 // divide it).
 #define MOE_STREAM_LAUNCH(KERNEL, ...)                                               \
     do {                                                                             \
-        static const int g = persistent_grid(KERNEL<__VA_ARGS__>);                   \
+        static DeviceCache cache_;                                                   \
+        const int g = per_device(cache_, [] { return persistent_grid(KERNEL<__VA_ARGS__>); }); \
         hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), dim3(g), dim3(256), 0, s, A, L);   \
     } while (0)
 
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
-    const bool split = MOE_STREAM_KS_GATEUP == 4 && A.H % (32 * 4 * kP) == 0;
+    const bool split = kKsGateup == 4 && A.H % (32 * 4 * kP) == 0;
     if (mb == 1 && A.H % (32 * kPG) == 0) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kPG, kNBG);
     else if (mb == 1) MOE_STREAM_LAUNCH(stream_gateup_kernel, 1, 1, kP, kNBG);
     else if (split) MOE_STREAM_LAUNCH(stream_gateup_kernel, 4, 4, kP, kNB);

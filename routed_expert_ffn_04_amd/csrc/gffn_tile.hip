@@ -342,17 +342,20 @@ hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm,
     (void)bm;
     switch (dt) {
         case DT_F32: {
-            static const int g = persistent_grid(tile_gateup_kernel<DT_F32>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_gateup_kernel<DT_F32>, 0); });
             hipLaunchKernelGGL(tile_gateup_kernel<DT_F32>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }
         case DT_BF16: {
-            static const int g = persistent_grid(tile_gateup_kernel<DT_BF16>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_gateup_kernel<DT_BF16>, 0); });
             hipLaunchKernelGGL(tile_gateup_kernel<DT_BF16>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }
         default: {
-            static const int g = persistent_grid(tile_gateup_kernel<DT_E4M3>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_gateup_kernel<DT_E4M3>, 0); });
             hipLaunchKernelGGL(tile_gateup_kernel<DT_E4M3>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }
@@ -364,17 +367,20 @@ hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, h
     (void)bm;
     switch (dt) {
         case DT_F32: {
-            static const int g = persistent_grid(tile_down_kernel<DT_F32>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_down_kernel<DT_F32>, 0); });
             hipLaunchKernelGGL(tile_down_kernel<DT_F32>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }
         case DT_BF16: {
-            static const int g = persistent_grid(tile_down_kernel<DT_BF16>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_down_kernel<DT_BF16>, 0); });
             hipLaunchKernelGGL(tile_down_kernel<DT_BF16>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }
         default: {
-            static const int g = persistent_grid(tile_down_kernel<DT_E4M3>, 0);
+            static DeviceCache c_;
+            const int g = per_device(c_, [] { return persistent_grid(tile_down_kernel<DT_E4M3>, 0); });
             hipLaunchKernelGGL(tile_down_kernel<DT_E4M3>, dim3(g), dim3(256), 0, s, A, L);
             break;
         }

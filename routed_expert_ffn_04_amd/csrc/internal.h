@@ -52,6 +52,9 @@ struct GffnProblem {
 };
 
 size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt);
+// Routed outputs as E4M3 codes (the FP8 combine) are written only by the
+// large e4m3 tiles, which need H % 256 == 0 and 32-bit row offsets.
+bool gffn_e4m3_y_supported(int H, int I, int R_max, int S);
 hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -147,3 +147,28 @@ def test_layer_validation():
     assert f(moe.F32, m4) == moe.MOE_ERR_UNSUPPORTED            # MXFP4 layers take bf16 x
     assert f(moe.BF16, m4, y_dt=2) == moe.MOE_ERR_UNSUPPORTED
     assert f(moe.BF16, m4, ws=128) == moe.MOE_ERR_WORKSPACE     # valid up to the workspace
+
+
+def test_e4m3_outputs_refused_where_the_large_tiles_do_not_run():
+    """E4M3 routed outputs (the FP8 combine) are written only by the 256-row
+    e4m3 tiles, which need 32-bit row offsets: a call whose R_max * H reaches
+    2^32 would fall back to the 64-row tiles, so it is refused before any
+    launch (the pointers here are dummies that a launch would fault on)."""
+    L = moe.lib()
+    H, I = 7168, 2048
+    e8 = _bank(8, H, I, moe.E4M3)
+    R_max = (1 << 32) // H + 1
+    st = L.moe_grouped_ffn(P, moe.E4M3, P, P, 8, P, 8, R_max, ctypes.byref(e8), None, None, 0, None,
+                           P, moe.E4M3, P, None, 0, P, 1 << 62, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    assert "E4M3 y" in moe.lib().moe_last_error().decode()
+    # just below the limit the same call is valid up to the workspace check
+    st = L.moe_grouped_ffn(P, moe.E4M3, P, P, 8, P, 8, (1 << 32) // H - 1, ctypes.byref(e8), None, None, 0, None,
+                           P, moe.E4M3, P, None, 0, P, 16, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    # the fused layer: T * k rows of y at H = 7168 reach 2^32 from T * k = 599,187
+    eb = _bank(256, H, I, moe.E4M3)
+    T = 599187 // 8 + 1
+    st = L.moe_layer(P, moe.BF16, T, H, P, None, 256, 8, 1, ctypes.byref(eb), None, P, moe.BF16, moe.E4M3,
+                     None, None, None, P, 1 << 62, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
