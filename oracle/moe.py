@@ -317,6 +317,34 @@ def moe_layer_tokens(wl, tokens) -> dict:
 
 # ----------------------------------------------------------- pre-routed groups
 
+def prerouted_rows(wl):
+    """The activation rows of a pre-routed grouped workload as the experts
+    consume them: a function of row indices giving fp64 rows [len][H].
+    e4m3 rows are codes with one fp32 scale per row and 128 columns, value =
+    e4m3(code) * scale[row][col / 128]; MXFP4 layers receive bf16 rows and
+    consume them as MXFP8 (quantised per 32 columns); bf16 / fp32 rows are
+    taken as they are."""
+    H = wl.H
+    if wl.w_dt == "e4m3":
+        qa = wl.a_q.cpu().numpy()
+        sa = wl.a_s.cpu().numpy().astype(np.float64)
+
+        def rows_of(idx):
+            idx = np.asarray(idx)
+            return (_E4M3_TABLE[qa[idx]].reshape(len(idx), H // 128, 128) * sa[idx][:, :, None]).reshape(len(idx), H)
+    elif wl.w_dt == "mxfp4":
+        xa = wl.x.float().cpu().numpy()
+
+        def rows_of(idx):
+            return mx.mxfp8_round_trip(xa[np.asarray(idx)])
+    else:
+        xa = wl.x.float().cpu().numpy()
+
+        def rows_of(idx):
+            return xa[np.asarray(idx)].astype(np.float64)
+    return rows_of
+
+
 def grouped_ffn(wl, group_sample=None) -> dict:
     """Pre-routed grouped FFN (no routing, no combine): each routed group g
     runs expert g on its contiguous rows, the shared expert on the last
@@ -327,23 +355,7 @@ def grouped_ffn(wl, group_sample=None) -> dict:
     H = wl.H
     G = len(wl.group_m)
     starts = np.concatenate([[0], np.cumsum(wl.group_m)]).astype(np.int64)
-    if wl.w_dt == "e4m3":
-        qa = wl.a_q.cpu().numpy()
-        sa = wl.a_s.cpu().numpy().astype(np.float64)
-
-        def rows_of(idx):
-            return (_E4M3_TABLE[qa[idx]].reshape(len(idx), H // 128, 128) * sa[idx][:, :, None]).reshape(len(idx), H)
-    elif wl.w_dt == "mxfp4":
-        # rows arrive as bf16 and are consumed as MXFP8 (quantised per 32 columns)
-        xa = wl.x.float().cpu().numpy()
-
-        def rows_of(idx):
-            return mx.mxfp8_round_trip(xa[idx])
-    else:
-        xa = wl.x.float().cpu().numpy()
-
-        def rows_of(idx):
-            return xa[idx].astype(np.float64)
+    rows_of = prerouted_rows(wl)
     res = {}
     segs = [(g, starts[g], wl.group_m[g]) for g in range(G)]
     if wl.shared_m:
