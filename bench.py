@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 import routed_expert_ffn_04_amd as moe  # noqa: E402
-from routed_expert_ffn_04_amd import accounting  # noqa: E402
+from measure import accounting  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "MoE layer tokens/s at 1 GPU; grouped-FFN HBM GB/s (T=128) and MFMA TFLOPS (T=16384)"
@@ -72,7 +72,7 @@ def dump_inputs(cid: int, out_dir: str, fp8_combine: bool = False, mxfp4: bool =
 
 def measured_record(name: str):
     """The stored counter record of a workload (profiles/traffic.json,
-    written by routed_expert_ffn_04_amd.traffic), or None when there is none
+    written by measure.traffic), or None when there is none
     or the kernel sources changed since it was taken."""
     path = os.path.join(HERE, "profiles", "traffic.json")
     try:

@@ -74,14 +74,13 @@ def _gffn_source(name: str) -> bool:
 
 def sources_digest() -> str:
     """sha256 over the sources of the grouped-FFN kernels and the C ABI
-    (csrc/, include/; see _gffn_source), in name order: the key that ties a
+    (routed_expert_ffn_04_amd/csrc/, include/; see _gffn_source), in name order: the key that ties a
     stored traffic measurement to the kernels it was taken on."""
     import hashlib
     import os
-    here = os.path.dirname(os.path.abspath(__file__))
-    root = os.path.dirname(here)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     h = hashlib.sha256()
-    for d in (os.path.join(here, "csrc"), os.path.join(root, "include")):
+    for d in (os.path.join(root, "routed_expert_ffn_04_amd", "csrc"), os.path.join(root, "include")):
         for name in sorted(os.listdir(d)):
             path = os.path.join(d, name)
             if os.path.isfile(path) and _gffn_source(name):

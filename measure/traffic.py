@@ -1,9 +1,11 @@
 """Measured HBM traffic of the grouped FFN per call, for the benchmark's
 roofline record.
 
-Run on a machine with the GPU (the parent process never touches it):
+Build the probe beside this file on any machine with hipcc, after the
+library (python -m measure.traffic --build), then run on a machine with the
+GPU (the parent process never touches it):
 
-    python -m routed_expert_ffn_04_amd.traffic --configs 2 5
+    python -m measure.traffic --configs 2 5
 
 For every workload it writes the routing inputs (bench.py --dump-inputs),
 then runs the native probe (no torch) on exactly that routing under two
@@ -35,9 +37,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 sys.path.insert(0, ROOT)
 
-from routed_expert_ffn_04_amd.accounting import sources_digest  # noqa: E402
+from measure.accounting import sources_digest  # noqa: E402
 
 PROBE = os.path.join(HERE, "moe_probe")
+LIBDIR = os.path.join(ROOT, "routed_expert_ffn_04_amd")
+
+
+def build_probe() -> str:
+    """Compile moe_probe.cpp against the built library (hipcc, gfx950)."""
+    from routed_expert_ffn_04_amd import build as libbuild
+    cmd = [libbuild.HIPCC, *libbuild.FLAGS, "-I", libbuild.INCLUDE, os.path.join(HERE, "moe_probe.cpp"),
+           "-o", PROBE + ".tmp", "-L", LIBDIR, "-lmoe_gfx950", "-Wl,-rpath,$ORIGIN/../routed_expert_ffn_04_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"moe_probe build failed:\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
 GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::mxbig_kernel", "moe::gffn_build_lists")
 XCDS = 8          # MI355X accelerator dies
 NAMES = {
@@ -97,7 +112,13 @@ def main():
     ap.add_argument("--calls", type=int, default=2, help="timed calls per probe run (one more is the warm-up)")
     ap.add_argument("--work", default="/tmp/moe_traffic", help="scratch (dumped inputs, raw counter files)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--build", action="store_true", help="only compile the probe (no GPU needed)")
     args = ap.parse_args()
+    if args.build:
+        print(build_probe())
+        return
+    if not os.path.exists(PROBE):
+        raise SystemExit(f"{PROBE} is missing: build it first (python -m measure.traffic --build)")
     os.makedirs(args.work, exist_ok=True)
     os.environ.setdefault("TMPDIR", "/tmp")
 
@@ -145,7 +166,7 @@ def main():
         rec["mfma_busy_cycles"] = round(busy / ncalls)
         rec["grbm_gui_active"] = round(active / ncalls)
         rec["mfma_busy_frac"] = round(busy / (active / XCDS * cus * 4), 4) if active else None
-        rec["command"] = (f"python -m routed_expert_ffn_04_amd.traffic --configs {' '.join(map(str, args.configs))}"
+        rec["command"] = (f"python -m measure.traffic --configs {' '.join(map(str, args.configs))}"
                           + (f" --fp8-combine-configs {' '.join(map(str, args.fp8_combine_configs))}"
                              if args.fp8_combine_configs else "")
                           + (f" --mxfp4-configs {' '.join(map(str, args.mxfp4_configs))}"

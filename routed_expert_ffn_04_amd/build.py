@@ -12,7 +12,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
-PROBE = os.path.join(HERE, "moe_probe")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -50,14 +49,6 @@ def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB, build_dir:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, lib_path)
-    if lib_path == LIB:
-        # native driver of the C ABI (counter runs without Python)
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, os.path.join(CSRC, "moe_probe.cpp"), "-o", PROBE + ".tmp",
-               "-L", HERE, "-lmoe_gfx950", "-Wl,-rpath,$ORIGIN"]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"moe_probe build failed:\n{r.stderr}")
-        os.replace(PROBE + ".tmp", PROBE)
     if verbose:
         print(lib_path)
     return lib_path

@@ -5,7 +5,7 @@ import os
 
 import pytest
 
-from routed_expert_ffn_04_amd import accounting
+from measure import accounting
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_expert_gemm_flops.json")))
 

@@ -8,7 +8,7 @@ import torch
 
 import bench
 import synth
-from routed_expert_ffn_04_amd import accounting
+from measure import accounting
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 5])
