@@ -229,6 +229,30 @@ size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, int3
                                 int32_t x_dt, int32_t w_dt, int32_t has_shared, int32_t out_dt,
                                 int32_t y_dt);
 
+/* ---- the whole layer without a workspace --------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): moe_layer
+ * with the same arguments and results, whose scratch is a 64 MiB device array
+ * inside the library (one per GPU, held until the process ends) instead of
+ * a caller workspace.  No allocation happens in the call.
+ *  - Calls needing more scratch than the array (moe_layer_workspace_size of
+ *    their sizes above 64 MiB; for the 7168 x 2048 x 256-expert layer with
+ *    bf16 weights: T above 400 with bf16 outputs, above 226 with fp32
+ *    outputs) return MOE_ERR_UNSUPPORTED before any launch.
+ *  - The array of a GPU is shared by every call on it and keeps the last
+ *    call's contents; nothing in it needs to start at zero (each call writes
+ *    every scratch value it reads).  Calls that overlap on one GPU (two host
+ *    threads, or two streams whose work runs concurrently) race on it and
+ *    give undefined results: order them on one stream or with events.
+ *  - `stream` must belong to the current device (else MOE_ERR_INVALID); the
+ *    array's address is looked up on the first call on each device. */
+moe_status_t moe_layer_noalloc(const void* x, int32_t x_dt, int32_t T, int32_t H,
+                               const float* w_router, const float* bias, int32_t E, int32_t k,
+                               int32_t score, const moe_experts_t* routed, const moe_experts_t* shared,
+                               void* out, int32_t out_dt, int32_t y_dt,
+                               int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                               void* stream);
+
 /* Name of a status code; text of the calling thread's last error ("" if none). */
 const char* moe_status_string(int32_t status);
 const char* moe_last_error(void);

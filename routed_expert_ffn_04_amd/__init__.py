@@ -6,7 +6,8 @@ kernels behind the C ABI declared in include/moe.h.  The library is loaded on
 first use and a missing library is an error (there is no fallback path).
 
 Entry points mirror the C ABI: route, permute, quant_e4m3_1x128,
-quant_mxfp8, grouped_ffn, combine, layer (plus workspace-size queries).
+quant_mxfp8, grouped_ffn, combine, layer, layer_noalloc (plus
+workspace-size queries).
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ SCORE = {"softmax": SOFTMAX, "sigmoid": SIGMOID}
 EXPORTS = [
     "moe_route", "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
     "moe_quant_e4m3_1x128", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
-    "moe_combine", "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error",
+    "moe_combine", "moe_layer", "moe_layer_workspace_size", "moe_layer_noalloc", "moe_status_string",
+    "moe_last_error",
 ]
 
 
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(ExpertsT),
                            ctypes.POINTER(ExpertsT), _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
             "moe_layer_workspace_size": ([_I32] * 10, _SZ),
+            "moe_layer_noalloc": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(ExpertsT),
+                                   ctypes.POINTER(ExpertsT), _P, _I32, _I32, _P, _P, _P, _P], _I32),
             "moe_status_string": ([_I32], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -300,4 +304,31 @@ def layer(x, w_router, bias, k: int, score: str, routed: Experts, shared: Option
                            ctypes.byref(rs), ctypes.byref(ss) if ss is not None else None,
                            _ptr(out), _dt_of(out), y_dt, _ptr(ids), _ptr(w), _ptr(counts),
                            _ptr(ws), ws.numel(), _stream(stream)))
+    return (out, ids, w, counts) if want_routing else out
+
+
+def layer_noalloc(x, w_router, bias, k: int, score: str, routed: Experts, shared: Optional[Experts] = None,
+                  out_dtype=None, out=None, want_routing: bool = False, stream=None, y_dtype=None):
+    """moe_layer_noalloc: the fused layer with the library's own static
+    scratch (no workspace argument, no device allocation by the library).
+    Outputs are allocated here unless `out` (and, with want_routing, the
+    routing buffers) are passed in."""
+    import torch
+    T, H = x.shape
+    E = w_router.shape[1]
+    rs = routed.struct()
+    ss = shared.struct() if shared is not None else None
+    out_dtype = out_dtype or torch.float32
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    ids = w = counts = None
+    if want_routing:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    y_dt = _dt_of(out) if y_dtype is None else (E4M3 if _is_fp8(y_dtype) else _dt_of(torch.empty(0, dtype=y_dtype)))
+    _check(lib().moe_layer_noalloc(_ptr(x), _dt_of(x), T, H, _ptr(w_router), _ptr(bias), E, k, SCORE[score],
+                                   ctypes.byref(rs), ctypes.byref(ss) if ss is not None else None,
+                                   _ptr(out), _dt_of(out), y_dt, _ptr(ids), _ptr(w), _ptr(counts), _stream(stream)))
     return (out, ids, w, counts) if want_routing else out

@@ -60,6 +60,16 @@ moe::Bank to_bank(const moe_experts_t* b) {
 
 }  // namespace
 
+namespace moe {
+int set_error(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_string(int32_t st) {

@@ -8,6 +8,9 @@
 
 namespace moe {
 
+// api.cpp: sets the calling thread's error text (moe_last_error) and returns status
+int set_error(int status, const char* fmt, ...);
+
 // route.hip
 hipError_t launch_router_logits(const void* x, int x_bf16, int T, int H, const float* wr,
                                 const float* bias, int E, float* logits, hipStream_t s);
