@@ -63,14 +63,20 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
 // are taken by the accumulators).
 struct Loader {
     const uint8_t* base;   // wave-uniform
-    const float* sbase;    // e4m3, waves 0-3: wave-uniform base of the activation scales
-    uint32_t soff;         // e4m3, waves 0-3: byte offset of row 64 w + l's scales
 };
+
+// Offsets of a lane's loads are kept in LDS as pairs (q even, q odd) so that
+// one 8-byte read brings the two loads issued together.
+__device__ __forceinline__ int loff_index(int q, int tid) { return ((q >> 1) * 512 + tid) * 2 + (q & 1); }
+
+__device__ __forceinline__ void issue_at(uint8_t* lds_stage, const Loader& ld, uint32_t off, int k0, int wave, int q) {
+    __builtin_amdgcn_global_load_lds((const void*)(ld.base + k0 + off), (lds_void*)(lds_stage + (wave * 8 + q) * 1024),
+                                     16, 0, 0);
+}
 
 __device__ __forceinline__ void issue_one(uint8_t* lds_stage, const Loader& ld, const uint32_t* loff, int k0, int wave,
                                           int tid, int q) {
-    __builtin_amdgcn_global_load_lds((const void*)(ld.base + k0 + loff[q * 512 + tid]),
-                                     (lds_void*)(lds_stage + (wave * 8 + q) * 1024), 16, 0, 0);
+    issue_at(lds_stage, ld, loff[loff_index(q, tid)], k0, wave, q);
 }
 
 // 32-byte e4m3 fragment (16x16x128 operand) of the 16 rows starting at row0
@@ -96,37 +102,191 @@ __device__ __forceinline__ bf16x8 frag16(const uint8_t* base, int row, int lane,
     return *(const bf16x8*)(base + swz(row, ks * 2 + lane / 32));
 }
 
-// position of token t = 128 wm + 16 i + c's scale product within a
-// 256-entry kind block: [wm][i / 4][c][i % 4], so that the 16 lanes reading
-// one quarter read 256 contiguous bytes
-__device__ __forceinline__ int prod_index(int t) {
-    return (t & ~127) + ((t & 127) >> 6) * 64 + (t & 15) * 4 + (((t & 127) >> 4) & 3);
-}
-
 struct BigSmem {
     uint8_t* stage_buf;           // 2 x 64 KiB
     uint32_t* aoff;               // 256 A-row byte offsets from the A base
     int* out_row;                 // 256 output rows (-1: none)
     const float** srow;           // 256 activation-scale rows (e4m3)
-    float* sprod;                 // [2 stages][2][256] scale products
+    float* sprod;                 // [2 stages][256 tokens][2 kinds] scale products
     float* red;                   // [4][256] amax partials
-    uint32_t* loff;               // [8][512] per-thread chunk offsets of the direct loads
-    float* sa_lds;                // [2][256] activation scales of a later stage (e4m3)
-    float* w_lds;                 // [2][64] weight scales of a later stage (e4m3): [0], [1]
+    uint32_t* loff;               // [4][512][2] per-thread chunk offsets of the direct loads (loff_index)
 };
 
-// Direct loads of the scales of K block kb into LDS slot kb & 1 (e4m3):
-// waves 0-3 the activation scale of their 64 rows, wave 4 the two weight
-// scales (lane l: the first block's if l is even, else the second's).
-__device__ __forceinline__ void issue_scales(const BigSmem& S, const Loader& ld, const float* w0, const float* w1,
-                                             int kb, int wave, int lane) {
-    if (wave < 4) {
-        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)(ld.sbase + kb) + ld.soff),
-                                         (lds_void*)(S.sa_lds + (kb & 1) * kBigM + wave * 64), 4, 0, 0);
-    } else if (wave == 4) {
-        __builtin_amdgcn_global_load_lds((const void*)((lane & 1 ? w1 : w0) + kb), (lds_void*)(S.w_lds + (kb & 1) * 64),
-                                         4, 0, 0);
+// Promotion of one MFMA's partial products (a 16 x 16 block over a 128-wide K
+// block) into the fp32 accumulators: acc += partial * (activation scale x
+// weight scale).  c holds the lane's token's products with the two
+// weight-scale kinds (gate/up: gate for weight blocks j < 2, up for j >= 2;
+// down: the wave's 128-column block, the second one for wn >= 2).
+template <int PHASE>
+__device__ __forceinline__ void promote1(f32x4& acc, const f32x4& t, float2 c, int j, int wn) {
+    const float cj = PHASE == 0 ? (j < 2 ? c.x : c.y) : (wn >= 2 ? c.y : c.x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(t[q], cj, acc[q]);
+}
+
+// Scheduling groups of one block of the e4m3 K loop (the builtin takes
+// literal arguments only; the branches fold away once the block loop is
+// unrolled): nds LDS reads first, then four times one MFMA followed by four
+// VALU instructions, then (dma) two direct loads.
+__device__ __forceinline__ void sched_block_order(int nds, bool dma) {
+    if (nds == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (nds == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
+    if (dma) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+}
+
+// One K stage of the e4m3 tile for one wave: D^T = W X^T, the MFMA row
+// operand a 16-column weight block, the column operand a 16-token block; a
+// lane accumulates columns 4 (l/16) + q of the weight block for token l%16.
+// The wave computes its first NB 16-row token blocks (8 in full tiles; in the
+// last, partial m-tile of a group the number of blocks holding rows, rounded
+// up to 1, 2, 4 or 8: rows past the group's end re-read its last row and are
+// never stored, so computing them is harmless).
+//
+// Software pipeline over the stage's MFMAs n = 4 i + j (token block i, weight
+// block j): MFMA n writes its partial into T[j] of a four-deep ring, and the
+// partial of MFMA n - 3 is promoted right after it is issued, so no FMA waits
+// on the MFMA just issued.  The last three partials of a stage (block NB-1,
+// j = 1..3) are promoted after the next stage's first MFMAs (cp: their scale
+// pair).  The next block's token fragment is read one block ahead.  The
+// stage's scale pairs are read before any direct load is issued (an LDS read
+// placed after a direct load may be made to wait for it).  With MORE the next
+// stage's direct loads go out two at a time after blocks 1-4 (after the last
+// block when there are fewer); NB and MORE are template parameters so that the
+// block sequence has no branch for the compiler to move the MFMAs across.
+template <int PHASE, int NB, bool MORE>
+__device__ __forceinline__ void fp8_stage(f32x4 (&acc8)[8][4], f32x4 (&T)[4], float2& cp, const BigSmem& S,
+                                          const Loader& ld, const uint8_t* cur, uint8_t* nbuf, int k1, int s, int tid,
+                                          int lane, int wave, int wm, int wn) {
+    const uint8_t* As = cur;
+    const uint8_t* Bs = cur + kBigM * kStage;
+    const Frag8Lane fl = frag8_lane(lane);
+    auto dma_pair = [&](int p) {   // loads 2p and 2p+1 of the next stage
+        const uint32_t o0 = S.loff[loff_index(2 * p, tid)];
+        const uint32_t o1 = S.loff[loff_index(2 * p + 1, tid)];
+        issue_at(nbuf, ld, o0, k1, wave, 2 * p);
+        issue_at(nbuf, ld, o1, k1, wave, 2 * p + 1);
+    };
+    if constexpr (NB > 0) {
+        // scale pairs of this lane's token in the wave's token blocks
+        const float2* sp2 = (const float2*)(S.sprod + (s & 1) * 2 * kBigM) + wm * 128 + lane % 16;
+        float2 c[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) c[i] = sp2[i * 16];
+        // weight blocks j: gate/up j<2 gate columns wn*32+16j, j>=2 up columns; down wn*64+16j
+        i32x8 wfr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2)) : wn * 64 + 16 * j;
+            wfr[j] = frag8(Bs, brow, fl);
+        }
+        i32x8 x = frag8(As, wm * 128, fl);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            i32x8 xn = x;
+            if (i + 1 < NB) xn = frag8(As, wm * 128 + (i + 1) * 16, fl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                T[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], x, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                         127, 0, 127);
+                if (j == 3)
+                    promote1<PHASE>(acc8[i][0], T[0], c[i], 0, wn);
+                else if (i > 0)
+                    promote1<PHASE>(acc8[i - 1][j + 1], T[j + 1], c[i - 1], j + 1, wn);
+                else   // the previous stage's last block (zero partials before the first stage)
+                    promote1<PHASE>(acc8[NB - 1][j + 1], T[j + 1], cp, j + 1, wn);
+            }
+            if (MORE && i >= 1 && i < 5) dma_pair(i - 1);
+            x = xn;
+            // the block's order: its LDS reads, then each MFMA followed by the
+            // four promotion FMAs of the partial three MFMAs back (so the FMAs
+            // run while the matrix core works), then its direct loads
+            sched_block_order((i + 1 < NB ? 2 : 0) + (MORE && i >= 1 && i < 5 ? 2 : 0), MORE && i >= 1 && i < 5);
+            // keep the scheduler from hoisting later blocks' fragment reads
+            // (register pressure: the accumulators take half the budget)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cp = c[NB - 1];
+    }
+    if constexpr (MORE) {
+#pragma unroll
+        for (int p = NB > 1 ? (NB - 1 < 4 ? NB - 1 : 4) : 0; p < 4; ++p) dma_pair(p);
+    }
+}
+
+// The K loop of an e4m3 tile for a wave computing NB token blocks.  Scale
+// products: activation scale of the row x weight scale of the column block,
+// per row and K block, for the first (gate) and second (up) column block,
+// stored per token as a (kind 0, kind 1) pair.  Stage s's products are
+// written by waves 0-3 at the start of stage s-1 from scales loaded into
+// registers one stage earlier (the row's activation scale by its thread, the
+// two weight scales into scalar registers), so their latency hides behind a
+// stage of compute; stage 0's come straight from memory at the tile start.
+// (Bringing the scales in with direct-to-LDS loads instead makes the compiler
+// wait for those loads before the stage's next LDS read.)  The last stage is
+// peeled off the loop (it issues no loads), so the loop body is one straight
+// sequence.
+template <int PHASE, int NB>
+__device__ __forceinline__ void fp8_kloop(f32x4 (&acc8)[8][4], const BigSmem& S, const Loader& ld, const float* wsc0,
+                                          const float* wsc1, int nstages, int tid, int lane, int wave, int wm, int wn) {
+    // global-address-space views: a generic load would count against the LDS
+    // counter too and make the next LDS reads wait for it
+    typedef const __attribute__((address_space(1))) float gfloat;
+    gfloat* srow = tid < kBigM ? (gfloat*)S.srow[tid] : nullptr;
+    gfloat* ws0 = (gfloat*)wsc0;
+    gfloat* ws1 = (gfloat*)wsc1;
+    float sa_n = 0.f, w_n0 = 0.f, w_n1 = 0.f;   // scales of the next products
+    if (tid < kBigM) {
+        const float sa0 = srow[0];
+        ((float2*)S.sprod)[tid] = make_float2(sa0 * ws0[0], sa0 * ws1[0]);
+    }
+    if (1 < nstages) {
+        if (tid < kBigM) sa_n = srow[1];
+        w_n0 = ws0[1];
+        w_n1 = ws1[1];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) issue_one(S.stage_buf, ld, S.loff, 0, wave, tid, q);
+
+    // ring of MFMA partials and the scale pair of the last block of the
+    // previous stage (zero before the first stage, so its promotion adds 0)
+    f32x4 T[4] = {};
+    float2 cp = make_float2(0.f, 0.f);
+    // stage start: this wave's direct loads of stage s (and the scale loads
+    // issued one stage earlier) landed (the barrier alone does not wait for
+    // direct loads), then every wave's; stage s-1 fully consumed.  Then the
+    // products of stage s+1 (into the buffer last read in stage s-1) and the
+    // scale loads of stage s+2.
+    auto top = [&](int s) {
+        wait_vm<0>();
+        __syncthreads();
+        if (s + 1 < nstages) {
+            if (tid < kBigM)
+                ((float2*)(S.sprod + ((s + 1) & 1) * 2 * kBigM))[tid] = make_float2(sa_n * w_n0, sa_n * w_n1);
+            if (s + 2 < nstages) {
+                if (tid < kBigM) sa_n = srow[s + 2];
+                w_n0 = ws0[s + 2];
+                w_n1 = ws1[s + 2];
+            }
+        }
+    };
+    int s = 0;
+    for (; s + 1 < nstages; ++s) {
+        top(s);
+        fp8_stage<PHASE, NB, true>(acc8, T, cp, S, ld, S.stage_buf + (s & 1) * kStageBytes,
+                                   S.stage_buf + ((s + 1) & 1) * kStageBytes, (s + 1) * kStage, s, tid, lane, wave, wm,
+                                   wn);
+    }
+    top(s);
+    fp8_stage<PHASE, NB, false>(acc8, T, cp, S, ld, S.stage_buf + (s & 1) * kStageBytes, nullptr, 0, s, tid, lane,
+                                wave, wm, wn);
+    if constexpr (NB > 0)
+#pragma unroll
+        for (int j = 1; j < 4; ++j) promote1<PHASE>(acc8[NB - 1][j], T[j], cp, j, wn);
 }
 
 // One tile: K loop and epilogue.  FULL: all 256 rows hold data.
@@ -171,104 +331,37 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
             for (int j = 0; j < 2; ++j) acc16[i][j] = f32x16{};
     }
 
-    // Scale products (e4m3): activation scale of the row x weight scale of the
-    // column block, per row and K block, for the first (gate) and second (up)
-    // column block.  Stage s's products are formed by waves 0-3 at the start
-    // of stage s-1 from scales that direct loads brought into LDS during stage
-    // s-2; stage 0's come straight from memory at the tile start.
-    // Products are stored per token at [kind][prod_index(t)], so a lane reads
-    // the eight of its token column with two 16-byte loads.
-    if (FP8 && tid < kBigM) {
-        const float sa0 = S.srow[tid][0];
-        S.sprod[prod_index(tid)] = sa0 * wsc0[0];
-        S.sprod[kBigM + prod_index(tid)] = sa0 * wsc1[0];
-    }
-    if (FP8 && 1 < nstages) issue_scales(S, ld, wsc0, wsc1, 1, wave, lane);
+    if constexpr (FP8) {
+        if (FULL || nrb > 4) fp8_kloop<PHASE, 8>(acc8, S, ld, wsc0, wsc1, nstages, tid, lane, wave, wm, wn);
+        else if (nrb > 2) fp8_kloop<PHASE, 4>(acc8, S, ld, wsc0, wsc1, nstages, tid, lane, wave, wm, wn);
+        else if (nrb == 2) fp8_kloop<PHASE, 2>(acc8, S, ld, wsc0, wsc1, nstages, tid, lane, wave, wm, wn);
+        else if (nrb == 1) fp8_kloop<PHASE, 1>(acc8, S, ld, wsc0, wsc1, nstages, tid, lane, wave, wm, wn);
+        else fp8_kloop<PHASE, 0>(acc8, S, ld, wsc0, wsc1, nstages, tid, lane, wave, wm, wn);
+    } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) issue_one(S.stage_buf, ld, S.loff, 0, wave, tid, q);
-
-    for (int s = 0; s < nstages; ++s) {
-        const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
-        // this wave's direct loads of stage s and of block s+1's scales landed
-        // (the barrier alone does not wait for them), then every wave's;
-        // stage s-1 fully consumed
-        wait_vm<0>();
-        __syncthreads();
-        if (s + 1 < nstages) {
-            if (FP8 && tid < kBigM) {
-                // products of stage s+1 into buffer (s+1)&1, last read in stage s-1
-                const float sa = S.sa_lds[((s + 1) & 1) * kBigM + tid];
-                const float* w = S.w_lds + ((s + 1) & 1) * 64;
-                float* spn = S.sprod + ((s + 1) & 1) * 2 * kBigM;
-                spn[prod_index(tid)] = sa * w[0];
-                spn[kBigM + prod_index(tid)] = sa * w[1];
-            }
-            if (FP8 && s + 2 < nstages) issue_scales(S, ld, wsc0, wsc1, s + 2, wave, lane);
-        }
-        // The next stage's eight direct loads of this wave are spread over
-        // the compute, two after each of blocks 1-4 (e4m3) or after each of
-        // the first two k-steps (bf16): issued back to back they would stall
-        // the wave on a full load queue (the vector L1 keeps a bounded number
-        // of line misses in flight) before its first MFMA.  Measured for e4m3
-        // at T = 16384: after blocks 1-4 2-3% faster than after 0-3; after
-        // 2-5 the same as 0-3; after 3-6, four per block after 0-1, or one
-        // per block after 0-7, slower.
-        const bool more = s + 1 < nstages;
-        uint8_t* nbuf = S.stage_buf + ((s + 1) & 1) * kStageBytes;
-        const int k1 = (s + 1) * kStage;
-        auto dma2 = [&](int b) {   // loads 2b and 2b+1
-            if (more) {
-                issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b);
-                issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b + 1);
-            }
-        };
-        const uint8_t* As = cur;
-        const uint8_t* Bs = cur + kBigM * kStage;
-        if (FP8) {
-            // D^T = W X^T: the MFMA row operand is a 16-column weight block,
-            // the column operand a 16-token block; a lane accumulates columns
-            // 4 (l/16) + q of the weight block for token l%16.
-            const Frag8Lane fl = frag8_lane(lane);
-            // weight blocks j: gate/up j<2 gate columns wn*32+16j, j>=2 up columns; down wn*64+16j
-            i32x8 wfr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int brow = PHASE == 0 ? (j < 2 ? wn * 32 + 16 * j : 128 + wn * 32 + 16 * (j - 2)) : wn * 64 + 16 * j;
-                wfr[j] = frag8(Bs, brow, fl);
-            }
-            // scale products of this lane's token in the eight token blocks:
-            // gate/up: kind 0 (gate) for j<2, kind 1 (up) for j>=2; down: the
-            // kind of the wave's 128-column block (wn >= 2: the second)
-            const float* sp = S.sprod + (s & 1) * 2 * kBigM + wm * 128 + (lane % 16) * 4;
-            const int k0i = PHASE == 0 ? 0 : (wn >= 2 ? 1 : 0);
-            const f32x4 g0 = *(const f32x4*)(sp + k0i * kBigM);
-            const f32x4 g1 = *(const f32x4*)(sp + k0i * kBigM + 64);
-            f32x4 u0 = g0, u1 = g1;
-            if (PHASE == 0) {
-                u0 = *(const f32x4*)(sp + kBigM);
-                u1 = *(const f32x4*)(sp + kBigM + 64);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (FULL || i < nrb) {
-                    const i32x8 x = frag8(As, wm * 128 + i * 16, fl);
-                    const float cg = i < 4 ? g0[i & 3] : g1[i & 3];
-                    const float cu = i < 4 ? u0[i & 3] : u1[i & 3];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        const f32x4 tq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], x, z, 0, 0, 0, 127, 0, 127);
-                        const float c = (PHASE == 0 && j >= 2) ? cu : cg;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc8[i][j][q] = __builtin_fmaf(tq[q], c, acc8[i][j][q]);
-                    }
+        for (int q = 0; q < 8; ++q) issue_one(S.stage_buf, ld, S.loff, 0, wave, tid, q);
+        for (int s = 0; s < nstages; ++s) {
+            const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
+            // this wave's direct loads of stage s landed (the barrier alone
+            // does not wait for them), then every wave's; stage s-1 fully consumed
+            wait_vm<0>();
+            __syncthreads();
+            // The next stage's eight direct loads of this wave are spread over
+            // the compute, two after each of the first two k-steps: issued
+            // back to back they would stall the wave on a full load queue (the
+            // vector L1 keeps a bounded number of line misses in flight)
+            // before its first MFMA.
+            const bool more = s + 1 < nstages;
+            uint8_t* nbuf = S.stage_buf + ((s + 1) & 1) * kStageBytes;
+            const int k1 = (s + 1) * kStage;
+            auto dma2 = [&](int b) {   // loads 2b and 2b+1
+                if (more) {
+                    issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b);
+                    issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b + 1);
                 }
-                if (i >= 1 && i < 5) dma2(i - 1);
-                // keep the scheduler from hoisting later blocks' fragment reads
-                // (register pressure: the accumulators take half the budget)
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
+            };
+            const uint8_t* As = cur;
+            const uint8_t* Bs = cur + kBigM * kStage;
             // bf16: 32x32 blocks; B block j: gate/up j=0 gate rows wn*32.., j=1 up rows 128+wn*32..;
             // down: rows wn*64 + 32j
 #pragma unroll
@@ -442,8 +535,6 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
     S.sprod = (float*)(S.srow + kBigM);
     S.red = S.sprod + 2 * 2 * kBigM;
     S.loff = (uint32_t*)(S.red + 4 * kBigM);
-    S.sa_lds = (float*)(S.loff + 8 * 512);
-    S.w_lds = S.sa_lds + 2 * kBigM;
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // scalar: wave-uniform branches
@@ -501,11 +592,7 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int row = (wave * 8 + q) * 8 + lane / 8;
-                S.loff[q * 512 + tid] = S.aoff[row] + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
-            }
-            if (FP8) {
-                ld.sbase = (const float*)uniform_ptr(PHASE == 0 ? (gi.shared ? A.a_sh_scale : A.a_scale) : A.h_scale);
-                ld.soff = (uint32_t)((const uint8_t*)S.srow[wave * 64 + lane] - (const uint8_t*)ld.sbase);
+                S.loff[loff_index(q, tid)] = S.aoff[row] + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
             }
         } else {
             // gate/up: B rows 0..127 gate columns n0.., 128..255 up columns; down: columns n0..n0+255
@@ -516,7 +603,7 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
                 const int row = (wave * 8 + q) * 8 + lane / 8;   // 256 .. 511
                 const int j = row - kBigM;
                 const int nrow = n0 + (PHASE == 0 ? (j & 127) : j);
-                S.loff[q * 512 + tid] = (uint32_t)nrow * (uint32_t)(K * EB) + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
+                S.loff[loff_index(q, tid)] = (uint32_t)nrow * (uint32_t)(K * EB) + (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
             }
         }
 
@@ -526,16 +613,16 @@ __global__ __launch_bounds__(512) void big_kernel(GArgs A, TileList L) {
 }
 
 // LDS: 2 stages + 256 A-row offsets + 256 output rows + 256 scale rows + products + amax partials
-// + load offsets + staged scales
+// + load offsets
 constexpr size_t kBigLds = 2 * kStageBytes + kBigM * sizeof(uint32_t) + kBigM * sizeof(int) + kBigM * sizeof(void*) +
-                           2 * 2 * kBigM * sizeof(float) + 4 * kBigM * sizeof(float) + 8 * 512 * sizeof(uint32_t) +
-                           2 * kBigM * sizeof(float) + 2 * 64 * sizeof(float);
+                           2 * 2 * kBigM * sizeof(float) + 4 * kBigM * sizeof(float) + 8 * 512 * sizeof(uint32_t);
 
 template <int DT, int PHASE>
 static hipError_t launch_big_t(const GArgs& A, const TileList& L, hipStream_t s) {
     static DeviceCache cache;
     const int grid = per_device(cache, [] {
-        hipFuncSetAttribute((const void*)big_kernel<DT, PHASE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+        (void)hipFuncSetAttribute((const void*)big_kernel<DT, PHASE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)kBigLds);
         return device_cu_count();   // one 512-thread workgroup per CU (LDS-limited)
     });
     hipLaunchKernelGGL((big_kernel<DT, PHASE>), dim3(grid), dim3(512), kBigLds, s, A, L);
