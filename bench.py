@@ -9,7 +9,10 @@ grouped FFN (tile builder + gate/up kernel + down kernel) is the dominant call
 and its roofline fraction is reported against the MI355X peaks.
 
 Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped decode batch
-(T = 128, H = 7168, 256 routed experts + 1 shared, I = 2048, top-8, bf16).
+(T = 128, H = 7168, 256 routed experts + 1 shared, I = 2048, top-8, bf16),
+whose tokens/s is `value` and whose grouped-FFN HBM rate is `roofline`; the
+same run then times the T = 16384 fp8 layer (the metric's MFMA half) and
+reports it under "prefill_T16384" with its own roofline (fp8 MFMA peak).
 """
 from __future__ import annotations
 
@@ -330,6 +333,10 @@ def main():
                     help="routed expert outputs as e4m3 per 1x128 before the combine (fp8 layers)")
     ap.add_argument("--mxfp4", action="store_true",
                     help="the layer workload with MXFP4 expert weights (MXFP8 activations and h)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload, skip the T=16384 fp8 layer timed after it")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed steps of the T=16384 fp8 layer in the default run")
     args = ap.parse_args()
     if args.mxfp4 and (args.config not in (2, 3, 5) or args.fp8_combine):
         print("bench.py: --mxfp4 applies to the layer workloads 2, 3 and 5 (without --fp8-combine)", file=sys.stderr)
@@ -347,15 +354,46 @@ def main():
     moe.lib()
     dev = torch.device("cuda:0")
     cid = args.config
-    wl = build_inputs(cid, dev, args.mxfp4)
-    if args.fp8_combine and (cid == 4 or wl.w_dt != "e4m3"):
+    m = measure(cid, args.steps, args.warmup, dev, mxfp4=args.mxfp4, fp8_combine=args.fp8_combine)
+    wl, runner = m.pop("wl"), m.pop("runner")
+    res = {
+        "metric": METRIC, "value": m["value"], "unit": m["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": m["dtype"],
+        "data": "synthetic (seeded counter-based normals; random-init weights)", "config": m["config"],
+        "roofline": m["roofline"], "grouped_ffn": m["grouped_ffn"], "calls_ms": m["calls_ms"],
+        "gpu_clock": m["gpu_clock"],
+    }
+    if "grouped_ffn_scrubbed" in m:
+        res["grouped_ffn_scrubbed"] = m["grouped_ffn_scrubbed"]
+    if not args.no_cpu:
+        log("timing the CPU oracle baseline ...")
+        res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 1 else 64)
+    if cid == 2 and not args.mxfp4 and not args.no_prefill:
+        # the metric's second half: the grouped FFN's MFMA rate on the T = 16384
+        # fp8 layer, timed in the same run with its own roofline (fp8 MFMA peak)
+        del wl, runner, m
+        torch.cuda.empty_cache()
+        p = measure(5, args.prefill_steps, args.warmup, dev)
+        p.pop("wl"), p.pop("runner")
+        res["prefill_T16384"] = {k: p[k] for k in ("config", "dtype", "value", "unit", "ms_per_step", "roofline",
+                                                   "grouped_ffn", "calls_ms", "gpu_clock")}
+        res["prefill_T16384"]["steps"] = args.prefill_steps
+    print(json.dumps(res), flush=True)
+
+
+def measure(cid: int, steps: int, warmup: int, dev, mxfp4: bool = False, fp8_combine: bool = False) -> dict:
+    """Time workload cid through its C-ABI calls and work out the grouped
+    FFN's roofline fraction; returns the figures of one bench record."""
+    wl = build_inputs(cid, dev, mxfp4)
+    if fp8_combine and (cid == 4 or wl.w_dt != "e4m3"):
         print("bench.py: --fp8-combine applies to the fp8 layer workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.fp8_combine:
+    if fp8_combine:
         wl.y_dt = "e4m3"          # also what the CPU oracle baseline computes
-    runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev, fp8_combine=args.fp8_combine)
-    ms, per, wall = run_timed(runner, args.steps, args.warmup)
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; per call (ms): " +
+    runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev, fp8_combine=fp8_combine)
+    ms, per, wall = run_timed(runner, steps, warmup)
+    log(f"config {cid}: timed {steps} steps: {ms:.3f} ms/step; per call (ms): " +
         ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
 
     # algorithmic work of the grouped FFN
@@ -371,7 +409,7 @@ def main():
     rows = sum(group_rows) + shared_rows
     flops = accounting.ffn_flops(rows, wl.H, wl.I)
     nbytes = accounting.grouped_ffn_bytes(group_rows, shared_rows, wl.H, wl.I, a_dt, wl.w_dt,
-                                          "e4m3" if args.fp8_combine else y_dt, y_dt)
+                                          "e4m3" if fp8_combine else y_dt, y_dt)
     gffn_ms = per["grouped_ffn"]
     gbs = nbytes / (gffn_ms * 1e-3) / 1e9
     tfs = flops / (gffn_ms * 1e-3) / 1e12
@@ -382,7 +420,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_TFLOPS[wl.w_dt], "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_TFLOPS[wl.w_dt], 4), "traffic": None}
-    rec = measured_record(wl.name + ("+fp8-combine" if args.fp8_combine else ""))
+    rec = measured_record(wl.name + ("+fp8-combine" if fp8_combine else ""))
     roof["traffic"] = None if rec is None else int(rec["bytes"])
     # matrix-core busy fraction of the same kernels (SQ_VALU_MFMA_BUSY_CYCLES), from the counter runs
     roof["mfma_busy"] = None if rec is None else rec.get("mfma_busy_frac")
@@ -401,30 +439,25 @@ def main():
     else:
         cfg.update(T=wl.T, E=wl.E, k=wl.k, shared=int(wl.shared is not None), score=wl.score,
                    bias="zipf1.2" if wl.bias is not None else None, x=wl.x_dt, out=wl.out_dt,
-                   y="e4m3 (fp8 combine)" if args.fp8_combine else wl.out_dt,
+                   y="e4m3 (fp8 combine)" if fp8_combine else wl.out_dt,
                    experts_touched=sum(1 for c in group_rows if c > 0))
     res = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
+        "value": round(value, 2), "unit": unit, "ms_per_step": round(ms, 4),
         "dtype": {"bf16": "bf16", "e4m3": "fp8-e4m3", "f32": "f32", "mxfp4": "mxfp4 x mxfp8"}[wl.w_dt],
-        "data": "synthetic (seeded counter-based normals; random-init weights)", "config": cfg,
-        "roofline": roof,
+        "config": cfg, "roofline": roof,
         "grouped_ffn": {"ms": round(gffn_ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)},
         "calls_ms": {k: round(v, 4) for k, v in per.items()},
         "gpu_clock": getattr(runner, "clock", None),
+        "wl": wl, "runner": runner,
     }
     if cid in (1, 4):
         # small working sets: also the call with caches scrubbed before each repetition
-        sms = scrubbed_ms(runner, args.steps, dev)
+        sms = scrubbed_ms(runner, steps, dev)
         res["grouped_ffn_scrubbed"] = {"ms": round(sms, 4), "GB/s": round(nbytes / (sms * 1e-3) / 1e9, 1),
                                        "TFLOP/s": round(flops / (sms * 1e-3) / 1e12, 2),
                                        "note": "512 MB write before each call (outside the timed call)"}
         log(f"grouped FFN with caches scrubbed: {sms:.4f} ms")
-    if not args.no_cpu:
-        log("timing the CPU oracle baseline ...")
-        res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 1 else 64)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":
