@@ -39,9 +39,12 @@ _lib = None
 def _router_lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_ROUTER_LIB):
-            _build_router(force=True)
-        _lib = ctypes.CDLL(_ROUTER_LIB)
+        path = os.environ.get("MOE_ORACLE_ROUTER_LIB")   # another build of router_chain.c (sanitizer runs)
+        if not path:
+            path = _ROUTER_LIB
+            if not os.path.exists(path):
+                _build_router(force=True)
+        _lib = ctypes.CDLL(path)
         _lib.oracle_router_logits.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_void_p]
@@ -286,12 +289,18 @@ def moe_layer(wl, want_intermediates: bool = False) -> dict:
     return res
 
 
-def moe_layer_tokens(wl, tokens) -> dict:
+def moe_layer_tokens(wl, tokens, procs: int = 1) -> dict:
     """Outputs for a subset of tokens only.  A token's routing and output
     depend on that token alone (the permutation only reorders work), so each
     sampled output is computed directly: out[t] = y_sh(x_t) +
     sum_j w[t][j] y_{ids[t][j]}(x_t).  Experts are visited one at a time
-    (only one expert's weights are held on the host at once)."""
+    (only one expert's weights are held on the host at once).
+
+    procs > 1 spreads the experts (and the shared expert) over that many
+    single-threaded worker processes (fork, no exec); every expert's rows are
+    computed by the same code either way, and the combine below is the same,
+    so the result does not depend on procs.  The banks are copied to host
+    memory first (the workers never touch a device)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x32, wr, b = layer_inputs(wl)
     xs = x32[tokens]
@@ -300,19 +309,63 @@ def moe_layer_tokens(wl, tokens) -> dict:
     hm = h_mode_for(wl.w_dt)
     y_dt = "bf16" if wl.out_dt == "bf16" else "f32"
     yr_dt = wl.y_dt or y_dt
-    out = np.zeros((len(tokens), wl.H))
+    # tasks: (key, bank, expert, token rows, output rounding)
+    tasks = []
     if wl.shared is not None:
-        out += round_to(expert_ffn(a, *bank_expert_f64(wl.shared, 0), hm), y_dt)
-    ys = {}
+        tasks.append(("shared", "shared", 0, np.arange(len(tokens)), y_dt))
     for e in sorted(set(int(e) for e in ids.reshape(-1))):
         rows_t, rows_j = np.nonzero(ids == e)
-        ye = round_y(expert_ffn(a[rows_t], *bank_expert_f64(wl.routed, e), hm), yr_dt)
-        for r, (t, j) in enumerate(zip(rows_t, rows_j)):
-            ys[(t, j)] = ye[r]
+        tasks.append(((e, rows_t, rows_j), "routed", e, rows_t, yr_dt))
+    banks = {"routed": wl.routed, "shared": wl.shared}
+    if procs > 1:
+        results = _map_experts(banks, a, hm, tasks, procs)
+    else:
+        results = [_expert_task(banks, a, hm, t) for t in tasks]
+    out = np.zeros((len(tokens), wl.H))
+    ys = {}
+    for (key, _, _, _, _), y in zip(tasks, results):
+        if key == "shared":
+            out += y
+        else:
+            _, rows_t, rows_j = key
+            for r, (t, j) in enumerate(zip(rows_t, rows_j)):
+                ys[(t, j)] = y[r]
     for t in range(len(tokens)):          # combine in slot order j = 0 .. k-1
         for j in range(wl.k):
             out[t] += np.float64(w[t, j]) * ys[(t, j)]
     return dict(tokens=tokens, ids=ids, w=w, out=round_to(out, wl.out_dt))
+
+
+def _expert_task(banks, a, hm, task):
+    """One expert's FFN on its token rows, rounded as the combine receives
+    it (routed: round_y; shared: round_to)."""
+    key, which, e, rows, rdt = task
+    y = expert_ffn(a[rows], *bank_expert_f64(banks[which], e), hm)
+    return round_to(y, rdt) if which == "shared" else round_y(y, rdt)
+
+
+_FORKED = {}   # state the forked workers inherit
+
+
+def _forked_task(i):
+    from threadpoolctl import threadpool_limits
+    st = _FORKED
+    with threadpool_limits(limits=1):
+        return _expert_task(st["banks"], st["a"], st["hm"], st["tasks"][i])
+
+
+def _map_experts(banks, a, hm, tasks, procs):
+    """_expert_task over tasks in `procs` forked processes (largest first)."""
+    import multiprocessing as mp
+    host = {k: (None if v is None else v.to("cpu")) for k, v in banks.items()}
+    _FORKED.update(banks=host, a=a, hm=hm, tasks=tasks)
+    order = sorted(range(len(tasks)), key=lambda i: -len(tasks[i][3]))
+    try:
+        with mp.get_context("fork").Pool(procs) as pool:
+            done = dict(zip(order, pool.map(_forked_task, order, chunksize=1)))
+    finally:
+        _FORKED.clear()
+    return [done[i] for i in range(len(tasks))]
 
 
 # ----------------------------------------------------------- pre-routed groups

@@ -17,7 +17,9 @@ from dataclasses import dataclass
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
+# MOE_GFX950_LIB names another build of the same library (the host-sanitizer
+# build the CPU tests run the boundary's argument checks under)
+LIB_PATH = os.environ.get("MOE_GFX950_LIB") or os.path.join(HERE, "libmoe_gfx950.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 F32, BF16, E4M3, MXFP4, MXFP8 = 0, 1, 2, 3, 4

@@ -6,8 +6,13 @@ Routing (expert ids) and the permutation (counts, offsets, src, dest) are
 compared bit-exactly over every token against the oracle; routing weights
 within 1e-6.  Layer outputs are compared on sampled tokens (or, for the
 pre-routed workload, sampled rows of every group) that the oracle computes one
-by one: max-abs <= 2e-2 and rel-Frobenius <= 1e-2 for fp32/bf16 weights,
-rel-Frobenius <= 3e-2 for fp8 weights.
+by one: max-abs <= 2e-2 and rel-Frobenius <= 1e-2 for fp32/bf16 weights; for
+fp8 weights (e4m3, MXFP4) rel-Frobenius <= 5e-3 and max-abs <= 2^-6 max|ref|
+(two bf16 spacings at the largest output).  The fp8 floor measured here is
+1e-3 to 2.4e-3: the outputs are bf16, and the matrix cores' fp8 sums differ
+from fp64 enough to move a few e4m3 codes of h per row and, through them,
+bf16 roundings of the outputs; a dropped 128-wide K block would move a row
+by 1/56 (gate/up) to 1/16 (down) of its norm.
 """
 import os
 import sys
@@ -35,7 +40,7 @@ def _check(got, ref, fp8, what):
     print(f"[{what}] rel_frob={rf:.3e} max_abs={ma:.3e} max|ref|={np.abs(ref).max():.3e}", flush=True)
     assert np.isfinite(got).all()
     if fp8:
-        assert rf <= 3e-2
+        assert rf <= 5e-3 and ma <= 2.0 ** -6 * np.abs(ref).max()
     else:
         assert rf <= 1e-2 and ma <= 2e-2
 
@@ -45,10 +50,9 @@ def _sample(T, n, seed):
     return sorted(set([0, T - 1] + rng.choice(T, size=n, replace=False).tolist()))
 
 
-@pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 16, False, False),
-                                                    (3, 6, False, False), (5, 4, False, False), (5, 3, True, False),
-                                                    (2, 16, False, True), (5, 3, False, True)])
-def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
+def _layer_run_and_routing(cid, fp8c, mxfp4):
+    """The layer through bench.LayerRunner at full size; routing and the
+    permutation checked bit-exactly over every token.  Returns (wl, run)."""
     print(f"config {cid}{' with the fp8 combine' if fp8c else ''}{' with MXFP4 weights' if mxfp4 else ''}: generating",
           flush=True)
     wl = synth.config_mxfp4(cid, device=DEV) if mxfp4 else synth.config(cid, device=DEV)
@@ -68,6 +72,13 @@ def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
     np.testing.assert_array_equal(run.offsets.cpu().numpy(), offsets)
     np.testing.assert_array_equal(run.src.cpu().numpy(), src)
     np.testing.assert_array_equal(run.dest.cpu().numpy(), dest)
+    return wl, run
+
+
+@pytest.mark.parametrize("cid,nsample,fp8c,mxfp4", [(1, None, False, False), (2, 16, False, False),
+                                                    (3, 6, False, False), (2, 16, False, True)])
+def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
+    wl, run = _layer_run_and_routing(cid, fp8c, mxfp4)
     out = run.out.float().cpu().numpy()
     fp8 = wl.w_dt in ("e4m3", "mxfp4")
     if nsample is None:
@@ -77,8 +88,67 @@ def test_layer_config_full_size(cid, nsample, fp8c, mxfp4):
         toks = _sample(wl.T, nsample, cid)
         print(f"config {cid}: oracle outputs for tokens {toks}", flush=True)
         ref = om.moe_layer_tokens(wl, toks)
-        np.testing.assert_array_equal(ref["ids"], ids_ref[toks])
+        np.testing.assert_array_equal(ref["ids"], run.ids.cpu().numpy()[toks])
         _check(out[toks], ref["out"], fp8, f"config {cid} tokens {toks}")
+
+
+# worker processes for the oracle's sampled outputs (its experts spread over
+# them); a dozen leaves the card's process budget and the host share alone
+ORACLE_PROCS = max(1, min(12, os.cpu_count() or 1))
+
+
+def _tail_tokens(offsets, src, k, n_min, seed):
+    """Sample tokens that reach every expert's last rows: the token of the
+    last row of each expert's segment (the high end of the segment, which
+    lies in the group's last, partial m-tile whenever the group spans more
+    than one), then random tokens up to n_min, plus tokens 0 and T-1."""
+    T = len(src) // k
+    toks = {0, T - 1}
+    for e in range(len(offsets) - 1):
+        if offsets[e + 1] > offsets[e]:
+            toks.add(int(src[offsets[e + 1] - 1]) // k)
+    rng = np.random.default_rng(seed)
+    while len(toks) < n_min:
+        toks.add(int(rng.integers(T)))
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("fp8c,mxfp4", [(False, False), (True, False), (False, True)])
+def test_prefill_layer_full_size_every_expert(fp8c, mxfp4):
+    """The T = 16384 fp8 layer (e4m3 weights; the same with the fp8 combine;
+    MXFP4 weights) at full size in the benchmark's launch configuration:
+    outputs of at least 256 tokens, among them for every expert the token of
+    its segment's last row, so every group's last m-tile (partial or full)
+    and every expert's weights are checked."""
+    wl, run = _layer_run_and_routing(5, fp8c, mxfp4)
+    out = run.out.float().cpu().numpy()
+    offsets = run.offsets.cpu().numpy()
+    src = run.src.cpu().numpy()
+    toks = _tail_tokens(offsets, src, wl.k, 256, 55)
+    covered = set(int(e) for e in run.ids.cpu().numpy()[toks].reshape(-1))
+    assert covered == set(range(wl.E))
+    print(f"config 5: oracle outputs for {len(toks)} tokens over {ORACLE_PROCS} processes", flush=True)
+    ref = om.moe_layer_tokens(wl, toks, procs=ORACLE_PROCS)
+    _check(out[toks], ref["out"], True, f"config 5 {len(toks)} tokens")
+
+
+@pytest.mark.parametrize("cid,fp8c,mxfp4", [(3, False, False), (5, False, False), (5, True, False),
+                                            (5, False, True)])
+def test_layer_full_size_all_tokens_deterministic(cid, fp8c, mxfp4):
+    """Two runs of the full-size layer give the same bits in every token's
+    output (and in the routed expert outputs)."""
+    wl = synth.config_mxfp4(cid, device=DEV) if mxfp4 else synth.config(cid, device=DEV)
+    wl.y_dt = "e4m3" if fp8c else None
+    run = bench.LayerRunner(wl, DEV, fp8_combine=fp8c)
+    outs, ys = [], []
+    for _ in range(2):
+        for _, f in run.calls():
+            f()
+        torch.cuda.synchronize()
+        outs.append(run.out.clone())
+        ys.append(run.y.clone())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(ys[0], ys[1])
 
 
 def test_grouped_config_full_size():

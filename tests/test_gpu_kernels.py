@@ -5,7 +5,13 @@ Bit-exact: expert ids, counts, offsets, src, dest, e4m3 codes and scales of
 activations.  Tolerances (written here, from the layer's accuracy target):
   routing weights            |dw| <= 1e-6
   fp32/bf16-weight outputs   max-abs <= 2e-2 and rel-Frobenius <= 1e-2
-  fp8-weight outputs         rel-Frobenius <= 3e-2
+  fp8-weight outputs         rel-Frobenius <= 1e-2
+The fp8 floor is set by the matrix cores' fp8 sums, which are not rounded
+like fp32 sums (about 2e-5 of the sum of the products' magnitudes on
+average, 2e-4 at most, per 128-long block): a few e4m3 codes of h per row,
+and of y when y is e4m3, land on the other side of a rounding boundary from
+the oracle's.  Observed up to ~5e-3 at these sizes (a flipped code weighs
+1/sqrt(I) of a row, I = 256 to 512), so the gate is twice that.
 """
 import numpy as np
 import pytest
@@ -22,7 +28,7 @@ DEV = "cuda:0"
 TOL_W = 1e-6
 TOL_MAXABS = 2e-2
 TOL_FROB = 1e-2
-TOL_FROB_FP8 = 3e-2
+TOL_FROB_FP8 = 1e-2
 
 
 def rel_frob(a, b):

@@ -2,10 +2,13 @@
 exponents, MXFP8 activations and h) against the CPU oracle.
 
 Bit-exact: MXFP8 codes and exponents of the activation quantisation.
-Expert and layer outputs: rel-Frobenius <= 3e-2 (the fp8 bar; the weights and
-activations are exact on both sides, so the residual is fp32 accumulation
-and the few h elements whose rounding decision flips between fp32 and the
-oracle's fp64)."""
+Expert and layer outputs: rel-Frobenius <= 1e-2.  The weights and
+activations are exact on both sides; the residual is the matrix cores' fp8
+sums, which are not rounded like fp32 sums (about 2e-5 of the sum of the
+products' magnitudes on average, 2e-4 at most, per 128-long block), and the
+h elements whose MXFP8 code flips because of it.  A flipped code moves a row
+of y by about 1/16 of one element over sqrt(I) of them: up to ~5e-3 here
+(I = 256), the gate twice that."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,7 @@ from oracle import moe as om
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL_FROB_FP8 = 3e-2
+TOL_FROB_FP8 = 1e-2
 
 
 def rel_frob(a, b):

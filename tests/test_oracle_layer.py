@@ -148,3 +148,19 @@ def test_grouped_prerouted_matches_direct_expert_ffn():
     y = moe.expert_ffn(a[130:135], wg, wu, wd, "e4m3")
     np.testing.assert_array_equal(r[1][1], codecs.bf16_rne(y))
     assert r["shared"][1].shape == (40, 256)
+
+
+@pytest.mark.parametrize("w_dt,y_dt", [("e4m3", None), ("e4m3", "e4m3"), ("mxfp4", None), ("bf16", None)])
+def test_forked_token_subset_matches_serial_and_full_layer(w_dt, y_dt):
+    """The multi-process token path (experts spread over forked workers) gives
+    the serial path's outputs bit for bit, and both the full layer's rows
+    (to library rounding: its products run over more rows at once)."""
+    wl = synth.make_layer(24, 256, 8, 2, 256, w_dt=w_dt, out_dt="bf16", seed=21)
+    wl.y_dt = y_dt
+    toks = [0, 3, 7, 11, 23]
+    serial = moe.moe_layer_tokens(wl, toks)
+    forked = moe.moe_layer_tokens(wl, toks, procs=3)
+    np.testing.assert_array_equal(forked["ids"], serial["ids"])
+    np.testing.assert_array_equal(forked["out"], serial["out"])
+    full = moe.moe_layer(wl)
+    np.testing.assert_allclose(serial["out"], full["out"][toks], rtol=1e-12, atol=1e-12)
