@@ -32,6 +32,9 @@ from measure import accounting  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "MoE layer tokens/s at 1 GPU; grouped-FFN HBM GB/s (T=128) and MFMA TFLOPS (T=16384)"
+# worker processes of the CPU oracle baseline (at most the host's cores): the
+# share of a host's CPUs that one GPU's job gets on an 8-GPU node
+CPU_PROCS = 16
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3,
                # fp8 x fp4 scaled MFMA: priced at the fp8 dense peak (the fp4 x fp4 rate is 10.1 PF)
@@ -282,13 +285,16 @@ def scrubbed_ms(runner, steps: int, dev, scrub_mb: int = 512):
 
 
 def cpu_baseline(wl, cid: int, sample_tokens: int):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload
-    (the oracle copies to the host only the experts its sample touches)."""
+    """The CPU oracle, as it stands, on a bounded sample of the same workload,
+    over the host's cores: its experts are spread over single-threaded forked
+    workers (the oracle copies to the host only the experts its sample
+    touches)."""
     import copy
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import moe as om
     oracle.build(force=False)
+    procs = max(1, min(CPU_PROCS, os.cpu_count() or 1))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         if cid == 4:
@@ -297,17 +303,13 @@ def cpu_baseline(wl, cid: int, sample_tokens: int):
             om.grouped_ffn(wl, group_sample=gs)
             n = sum(len(v) for v in gs.values())
             sample = f"first {sample_tokens} rows of each of the {len(gs)} groups"
-        elif sample_tokens >= wl.T:
-            om.moe_layer(wl)
-            n = wl.T
-            sample = f"whole workload ({wl.T} tokens)"
+            procs = 1
         else:
-            sub = copy.copy(wl)
-            sub.x = wl.x[:sample_tokens]
-            sub.T = sample_tokens
-            om.moe_layer_tokens(sub, list(range(sample_tokens)))
-            n = sample_tokens
-            sample = f"first {sample_tokens} of {wl.T} tokens (each token routed and run through its experts)"
+            T = min(sample_tokens, wl.T)
+            om.moe_layer_tokens(wl, list(range(T)), procs=procs)
+            n = T
+            sample = (f"whole workload ({wl.T} tokens)" if T == wl.T else
+                      f"first {T} of {wl.T} tokens (each token routed and run through its experts)")
         dt = time.perf_counter() - t0
     unit = "rows/s" if cid == 4 else "tokens/s"
     model = None
@@ -316,7 +318,7 @@ def cpu_baseline(wl, cid: int, sample_tokens: int):
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": round(n / dt, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+    return {"value": round(n / dt, 4), "unit": unit, "cores": procs, "kind": "oracle", "sample": sample,
             "seconds": round(dt, 2), "cpu_model": model}
 
 
@@ -327,7 +329,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the T=128 decode batch)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="tokens (rows) in the CPU oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens (rows) in the CPU oracle sample")
     ap.add_argument("--dump-inputs", metavar="DIR", help="write the workload's routing inputs for the native probe and exit")
     ap.add_argument("--fp8-combine", action="store_true",
                     help="routed expert outputs as e4m3 per 1x128 before the combine (fp8 layers)")
@@ -368,7 +370,7 @@ def main():
         res["grouped_ffn_scrubbed"] = m["grouped_ffn_scrubbed"]
     if not args.no_cpu:
         log("timing the CPU oracle baseline ...")
-        res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 1 else 64)
+        res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 4 else 16)
     if cid == 2 and not args.mxfp4 and not args.no_prefill:
         # the metric's second half: the grouped FFN's MFMA rate on the T = 16384
         # fp8 layer, timed in the same run with its own roofline (fp8 MFMA peak)

@@ -341,7 +341,7 @@ def _expert_task(banks, a, hm, task):
     it (routed: round_y; shared: round_to)."""
     key, which, e, rows, rdt = task
     y = expert_ffn(a[rows], *bank_expert_f64(banks[which], e), hm)
-    return round_to(y, rdt) if which == "shared" else round_y(y, rdt)
+    return round_to(y, rdt) if key == "shared" else round_y(y, rdt)
 
 
 _FORKED = {}   # state the forked workers inherit
@@ -355,10 +355,17 @@ def _forked_task(i):
 
 
 def _map_experts(banks, a, hm, tasks, procs):
-    """_expert_task over tasks in `procs` forked processes (largest first)."""
+    """_expert_task over tasks in `procs` forked processes (largest first).
+    The experts the tasks use are copied to host memory first, one bank of
+    one expert each, which the workers then read as expert 0."""
     import multiprocessing as mp
-    host = {k: (None if v is None else v.to("cpu")) for k, v in banks.items()}
-    _FORKED.update(banks=host, a=a, hm=hm, tasks=tasks)
+    host = {}
+    local = []
+    for key, which, e, rows, rdt in tasks:
+        if (which, e) not in host:
+            host[(which, e)] = banks[which].expert(e).to("cpu")
+        local.append((key, (which, e), 0, rows, rdt))
+    _FORKED.update(banks=host, a=a, hm=hm, tasks=local)
     order = sorted(range(len(tasks)), key=lambda i: -len(tasks[i][3]))
     try:
         with mp.get_context("fork").Pool(procs) as pool:

@@ -46,6 +46,7 @@ struct ListsOut {
 };
 
 constexpr int kMaxGroups = 1025;   // 1024 routed + shared
+constexpr int kSortSlots = 2048;   // power of two >= kMaxGroups; one compare per thread and pass
 
 // Exclusive scan of arr[0 .. n) in place by a 1024-thread workgroup (chunks of
 // 1024 with a running carry); returns the total.  Every thread must call it.
@@ -78,12 +79,13 @@ __device__ int block_scan_exclusive(int* arr, int n, int* wsum) {
 // One workgroup of 1024 threads.  Group g's rank inside its class is the
 // number of class members with more rows (or as many rows and a lower
 // index); each class's m-tiles are laid out in rank order, so the heaviest
-// groups come first.
+// groups come first.  The ranks come from one bitonic sort of the keys
+// (class, rows descending, group) over 2048 slots in LDS.
 __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restrict__ offsets, int G, int S,
                                                          int R_max, ClassSpec cs, ListsOut out) {
     __shared__ int m_of[kMaxGroups];
     __shared__ int cls_of[kMaxGroups];
-    __shared__ int2 mc_of[kMaxGroups];        // (m, class) packed for the rank loop
+    __shared__ unsigned long long keys[kSortSlots];   // class << 42 | (2^31 - 1 - m) << 11 | g; unused: ~0
     __shared__ int rank_of[kMaxGroups];
     __shared__ int nt_by_rank[kClasses][kMaxGroups];
     __shared__ int members[kClasses];
@@ -106,7 +108,6 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         c = m > 0 ? c : -1;
         m_of[g] = m;
         cls_of[g] = c;
-        mc_of[g] = make_int2(m, c);
         if (c >= 0) atomicAdd(&members[c], 1);
     }
     __syncthreads();
@@ -115,10 +116,7 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
                  : (cs.promote_min > 0 && m1 >= cs.promote_min)        ? 2 : 1;
     if (to != 1) {
         for (int g = tid; g < ng; g += 1024)
-            if (cls_of[g] == 1) {
-                cls_of[g] = to;
-                mc_of[g].y = to;
-            }
+            if (cls_of[g] == 1) cls_of[g] = to;
         __syncthreads();
         if (tid == 0) {
             members[to] += m1;
@@ -126,17 +124,33 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
         }
         __syncthreads();
     }
-    for (int g = tid; g < ng; g += 1024) {
-        const int c = cls_of[g];
-        if (c < 0) continue;
-        const int m = m_of[g];
-        int rank = 0;
-#pragma unroll 16
-        for (int o = 0; o < ng; ++o) {
-            const int2 mc = mc_of[o];
-            rank += (int)((mc.y == c) & ((mc.x > m) | ((mc.x == m) & (o < g))));
+    for (int i = tid; i < kSortSlots; i += 1024) {
+        const int c = i < ng ? cls_of[i] : -1;
+        keys[i] = c < 0 ? ~0ull
+                        : ((unsigned long long)c << 42) | ((unsigned long long)(0x7fffffff - m_of[i]) << 11) |
+                              (unsigned long long)i;
+    }
+    __syncthreads();
+    // ascending bitonic sort: thread t compares slot i (bit j of i clear) with i + j
+    for (int k = 2; k <= kSortSlots; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1));
+            const unsigned long long a = keys[i], b = keys[i + j];
+            if ((a > b) == ((i & k) == 0)) {
+                keys[i] = b;
+                keys[i + j] = a;
+            }
+            __syncthreads();
         }
-        nt_by_rank[c][rank] = (m + cs.bm[c] - 1) / cs.bm[c];
+    // a class's members are contiguous in the sorted order, heaviest first
+    for (int i = tid; i < kSortSlots; i += 1024) {
+        const unsigned long long key = keys[i];
+        if (key == ~0ull) continue;
+        const int c = (int)(key >> 42), g = (int)(key & 2047);
+        int first = 0;
+        for (int q = 0; q < c; ++q) first += members[q];
+        const int rank = i - first;
+        nt_by_rank[c][rank] = (m_of[g] + cs.bm[c] - 1) / cs.bm[c];
         rank_of[g] = rank;
     }
     __syncthreads();

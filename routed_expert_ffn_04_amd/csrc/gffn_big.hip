@@ -343,6 +343,10 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
     } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q) issue_one(S.stage_buf, ld, S.loff, 0, wave, tid, q);
+        // the lane's eight load offsets, the same in every stage of the tile
+        uint32_t lo[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lo[q] = S.loff[loff_index(q, tid)];
         for (int s = 0; s < nstages; ++s) {
             const uint8_t* cur = S.stage_buf + (s & 1) * kStageBytes;
             // this wave's direct loads of stage s landed (the barrier alone
@@ -359,29 +363,38 @@ __device__ __forceinline__ void big_tile(const GArgs& A, const GroupInfo& gi, co
             const int k1 = (s + 1) * kStage;
             auto dma2 = [&](int b) {   // loads 2b and 2b+1
                 if (more) {
-                    issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b);
-                    issue_one(nbuf, ld, S.loff, k1, wave, tid, 2 * b + 1);
+                    issue_at(nbuf, ld, lo[2 * b], k1, wave, 2 * b);
+                    issue_at(nbuf, ld, lo[2 * b + 1], k1, wave, 2 * b + 1);
                 }
             };
             const uint8_t* As = cur;
             const uint8_t* Bs = cur + kBigM * kStage;
             // bf16: 32x32 blocks; B block j: gate/up j=0 gate rows wn*32.., j=1 up rows 128+wn*32..;
-            // down: rows wn*64 + 32j
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 bfr[2];
+            // down: rows wn*64 + 32j.  The fragments of k-step ks+1 are read
+            // while the MFMAs of k-step ks run (two register sets), so no
+            // MFMA waits on the LDS read just issued.
+            bf16x8 af[2][4], bfr[2][2];
+            auto read_step = [&](int ks, bf16x8(&a)[4], bf16x8(&b)[2]) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int brow = PHASE == 0 ? (j == 0 ? wn * 32 : 128 + wn * 32) : wn * 64 + 32 * j;
-                    bfr[j] = frag16(Bs, brow + lane % 32, lane, ks);
+                    b[j] = frag16(Bs, brow + lane % 32, lane, ks);
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (FULL || 2 * i < nrb) a[i] = frag16(As, wm * 128 + i * 32 + lane % 32, lane, ks);
+            };
+            read_step(0, af[0], bfr[0]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks + 1 < 4) read_step(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (FULL || 2 * i < nrb) {
-                        const bf16x8 a = frag16(As, wm * 128 + i * 32 + lane % 32, lane, ks);
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[j], acc16[i][j], 0, 0, 0);
+                            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                                                  acc16[i][j], 0, 0, 0);
                     }
                 }
                 if (ks < 2) {

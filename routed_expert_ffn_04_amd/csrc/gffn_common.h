@@ -130,10 +130,12 @@ __device__ __forceinline__ int2 tile_coords(const TileList& L, long t, int ntn) 
 
 // s_waitcnt with only the vector-memory count: vmcnt(n), expcnt and
 // lgkmcnt left at their maxima (gfx9 encoding: vmcnt[3:0] | expcnt << 4 |
-// lgkmcnt << 8 | vmcnt[5:4] << 14).  A workgroup barrier (__syncthreads) does
-// not wait for this wave's direct global->LDS loads on gfx950: its fence
-// orders LDS operations only, so a barrier that hands such data to other
-// waves needs wait_vm<0>() (or a count) before it.
+// lgkmcnt << 8 | vmcnt[5:4] << 14).  The hardware barrier itself does not wait
+// for a wave's direct global->LDS loads; __syncthreads does, because the
+// compiler puts vmcnt(0) in front of its release fence (direct loads count as
+// LDS writes), so wait_vm<0>() before it only states the need.  A barrier
+// that must leave some loads in flight is an s_barrier after an explicit
+// count.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt");
