@@ -16,7 +16,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["route.hip", "permute.hip", "quant.hip", "combine.hip", "gffn.hip", "gffn_tile.hip",
-           "gffn_stream.hip", "gffn_big.hip", "gffn_mx.hip", "gffn_mxbig.hip", "noalloc.hip", "api.cpp"]
+           "gffn_stream.hip", "gffn_mid.hip", "gffn_big.hip", "gffn_mx.hip", "gffn_mxbig.hip", "noalloc.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

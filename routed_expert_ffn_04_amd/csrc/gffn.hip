@@ -6,7 +6,9 @@
 // Every group (routed expert g, plus the shared expert as group G) is put in
 // one of three tile classes by its row count m, read on the device:
 //   class 0: m <= 16          weight-streaming tiles of 16 rows   (bf16)
-//   class 1: 16 < m <= 256    weight-streaming tiles of 64 rows   (bf16)
+//   class 1: 16 < m <= 256    64 x 256 MFMA tiles with a three-stage load
+//                             ring (gffn_mid.hip) where the large tiles
+//                             apply, else weight-streaming tiles of 64 rows
 //   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
 //                             or 64-row LDS tiles (fp32 or H % 256 != 0)
 // (fp32 and e4m3 layers put every group in class 2; MXFP4 layers use the
@@ -37,6 +39,9 @@ struct ClassSpec {
     // handful of groups (the shared expert at decode) would otherwise run
     // alone in a launch that fills a fraction of the chip.  0: never.
     int demote_max;
+    // Class 1 runs the 64-row tiles with a three-stage load ring
+    // (gffn_mid.hip) instead of the weight-streaming tiles.
+    int mid1;
 };
 
 struct ListsOut {
@@ -220,10 +225,12 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
         c.demote_max = kDemoteMax;
         c.promote_min = big ? kPromoteMin : 0;
     } else if (dt == DT_BF16) {
+        // with the large tiles available (H % 256 == 0, 32-bit offsets), the
+        // mid-sized groups take the 64-row ring tiles, which share those limits
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
         c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
-        c.promote_min = bm2 == 256 ? kPromoteMin : 0;
+        c.mid1 = bm2 == 256;
         c.demote_max = kDemoteMax;
     } else {
         c.mlo[0] = 0;  c.mhi[0] = 0;        c.bm[0] = 16;   // unused
@@ -298,12 +305,14 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_gateup(A, up[k], s) : launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s))
+          : k == 1 && cs.mid1 ? launch_mid_gateup(A, up[k], s)
           : k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
                   : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
         if (me[k] == 0) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_down(A, dn[k], s) : launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s))
+          : k == 1 && cs.mid1 ? launch_mid_down(A, dn[k], s)
           : k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)
                   : cs.bm[k] == 256 ? launch_big_down(p.dt, A, dn[k], s) : launch_tile_down(p.dt, A, dn[k], cs.bm[k], s);
     }

@@ -142,12 +142,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_big.hip, gffn_mx.hip,
-// gffn_mxbig.hip).
+// Host launchers of the kernel families (gffn_tile.hip, gffn_stream.hip, gffn_mid.hip, gffn_big.hip,
+// gffn_mx.hip, gffn_mxbig.hip).
 hipError_t launch_tile_gateup(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_tile_down(int dt, const GArgs& A, const TileList& L, int bm, hipStream_t s);
 hipError_t launch_stream_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_stream_down(int mb, const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mid_gateup(const GArgs& A, const TileList& L, hipStream_t s);
+hipError_t launch_mid_down(const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_big_gateup(int dt, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_big_down(int dt, const GArgs& A, const TileList& L, hipStream_t s);
 hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream_t s);

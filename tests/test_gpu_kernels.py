@@ -159,10 +159,14 @@ GROUPED_CASES = [
     ([130, 5, 0, 64, 1], 40, 256, 256, "e4m3"),
     ([257, 9], 300, 512, 384, "e4m3"),
     ([70, 0, 12], 20, 256, 256, "f32"),
-    # 36 groups of 17..116 rows: enough 17..256-row groups to move them from
-    # the weight-streaming tiles to the 256-row tiles (and 31: just too few)
+    # 36 and 31 groups of 17..116 rows: the 64-row ring tiles (bf16, H % 256 == 0)
     ([17 + (g * 37) % 100 for g in range(36)], 50, 512, 256, "bf16"),
     ([17 + (g * 37) % 100 for g in range(31)] + [3, 0], 0, 512, 256, "bf16"),
+    # the 64-row ring tiles at their m-tile boundaries (one short, exact, one
+    # over), several m-tiles per group, the shared expert among them, and the
+    # shortest down K loop (I = 128: two stages)
+    ([17, 63, 64, 65, 128, 129, 192, 255, 256, 3], 100, 512, 128, "bf16"),
+    ([40, 90, 33, 250, 170], 0, 256, 256, "bf16"),
     # m-tile boundaries of the 256-row tiles: exact multiples, one short, one over
     ([256, 512, 255, 257, 1], 256, 512, 256, "e4m3"),
     ([256, 512, 255, 257, 1], 0, 512, 256, "bf16"),
