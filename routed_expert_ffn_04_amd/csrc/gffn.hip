@@ -6,7 +6,7 @@
 // Every group (routed expert g, plus the shared expert as group G) is put in
 // one of three tile classes by its row count m, read on the device:
 //   class 0: m <= 16          weight-streaming tiles of 16 rows   (bf16)
-//   class 1: 16 < m <= 256    32 x 256 MFMA tiles with a four-stage load
+//   class 1: 16 < m <= 256    64 x 256 MFMA tiles with a three-stage load
 //                             ring (gffn_mid.hip) where the large tiles
 //                             apply, else weight-streaming tiles of 64 rows
 //   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
@@ -39,7 +39,7 @@ struct ClassSpec {
     // handful of groups (the shared expert at decode) would otherwise run
     // alone in a launch that fills a fraction of the chip.  0: never.
     int demote_max;
-    // Class 1 runs the 32-row tiles with a four-stage load ring
+    // Class 1 runs the 64-row tiles with a three-stage load ring
     // (gffn_mid.hip) instead of the weight-streaming tiles.
     int mid1;
 };
@@ -228,7 +228,7 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
         // with the large tiles available (H % 256 == 0, 32-bit offsets), the
         // mid-sized groups take the 64-row ring tiles, which share those limits
         c.mlo[0] = 0;  c.mhi[0] = 16;       c.bm[0] = 16;
-        c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = bm2 == 256 ? 32 : 64;
+        c.mlo[1] = 16; c.mhi[1] = 256;      c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = 1 << 30; c.bm[2] = bm2;
         c.mid1 = bm2 == 256;
         c.demote_max = kDemoteMax;

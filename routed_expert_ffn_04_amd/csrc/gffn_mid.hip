@@ -1,4 +1,4 @@
-// Grouped expert FFN, 32-row tiles for bf16 groups of 17-256 rows.
+// Grouped expert FFN, 64-row tiles for bf16 groups of 17-256 rows.
 //
 // "DeepSeek V3/R1 Inference Efficiency (2)", section 1.b: grouped-GEMM
 // efficiency depends on the rows per group.  A group of a few dozen rows
@@ -6,17 +6,15 @@
 // those weights; the 256-row tiles of gffn_big.hip spend most of each stage's
 // loads on padding rows and keep only one 32 KiB weight stage in flight.
 //
-// Tile: 32 rows x 256 MFMA columns (gate/up: 128 gate + 128 up columns of the
+// Tile: 64 rows x 256 MFMA columns (gate/up: 128 gate + 128 up columns of the
 // same 128 h columns; down: 256 output columns), K staged 128 bytes (64 bf16)
-// at a time through a four-deep LDS ring (36 KiB a stage: 32 activation rows
-// then 256 weight rows) fed by direct global->LDS 16-byte loads, so three
-// stages (96 KiB of weights) are in flight while one is computed.  The rows
-// are XOR-swizzled as in the large tiles.  (64-row tiles with a three-deep
-// ring streamed the same groups 16% slower.)
-// 8 waves, each computing all 32 rows x 32 columns with
-// v_mfma_f32_16x16x32_bf16 (gate/up: 16 gate and the 16 up columns of the
-// same h columns, so SwiGLU needs no exchange); the matrix cores are far from
-// busy here, so the half-rate 16x16 form costs nothing.
+// at a time through a three-deep LDS ring (40 KiB a stage: 64 activation rows
+// then 256 weight rows) fed by direct global->LDS 16-byte loads, so two
+// stages (64 KiB of weights) are in flight while one is computed.  The rows
+// are XOR-swizzled as in the large tiles.
+// 8 waves (2 along M x 4 along N), each computing 32 x 64 with
+// v_mfma_f32_32x32x16_bf16, two per k-step (gate/up: the gate and the up
+// block of the same 32 h columns, so SwiGLU needs no exchange).
 // The m-tiles of a group that share a weight tile are adjacent in the tile
 // order (n-tile-major, m-tiles innermost), so a weight tile is read from HBM
 // once per die.
@@ -25,17 +23,17 @@
 namespace moe {
 namespace {
 
-constexpr int kM = 32;                        // rows per tile
+constexpr int kM = 64;                        // rows per tile
 constexpr int kN = 256;                       // MFMA columns per tile
 constexpr int kStage = 128;                   // K bytes per stage
 constexpr int kRows = kM + kN;                // LDS rows per stage
-constexpr int kStageBytes = kRows * kStage;   // 36 KiB
-constexpr int kRing = 4;                      // stages in the ring
-constexpr int kInstr = kRows / 8;             // 1 KiB direct-load instructions per stage: 36
-constexpr int kLoads = (kInstr + 7) / 8;      // per wave, at most: 5 (waves 0-3), 4 (waves 4-7)
-static_assert(kInstr == 8 * kLoads - 4, "waves 0-3 issue kLoads loads a stage, waves 4-7 one fewer");
+constexpr int kStageBytes = kRows * kStage;   // 40 KiB
+constexpr int kRing = 3;                      // stages in the ring
+constexpr int kLoads = kRows * 8 / kWave / 8; // direct loads per wave and stage (16 B per lane)
+static_assert(kLoads * kWave * 8 == kRows * 8, "loads cover the stage");
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kStage + ((chunk ^ swz_key(row)) << 4); }
@@ -45,6 +43,11 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte bf16 fragment (32x32x16 operand) of k-step ks: row, bytes [32 ks + 16 (lane/32), +16)
+__device__ __forceinline__ bf16x8 frag16(const uint8_t* base, int row, int lane, int ks) {
+    return *(const bf16x8*)(base + swz(row, ks * 2 + lane / 32));
 }
 
 // Workgroup barrier once this wave's LDS operations have completed and at
@@ -60,25 +63,21 @@ __device__ __forceinline__ void barrier_vm() {
     asm volatile("" ::: "memory");
 }
 
-// The direct loads of a stage: instruction q of wave w (q < nq(w): 5 for
-// waves 0-3, 4 for waves 4-7) is the stage's instruction first(w) + q, which
-// fills LDS rows 8 (first(w) + q) .. +7 (lane l: row + l/8, position l%8),
-// all from one matrix (activation rows below kM, weight rows above), so each
+// The direct loads of a stage: instruction q of wave w fills LDS rows
+// 8 (kLoads w + q) .. +7 (lane l: row + l/8, position l%8), all from one
+// matrix (activation rows below kM, weight rows above), so each
 // instruction's base address is wave-uniform.  off: the lane's byte offsets
 // from those bases, the same for every stage of a tile.
-__device__ __forceinline__ int first_instr(int wave) { return wave < 4 ? 5 * wave : 20 + 4 * (wave - 4); }
 struct Loads {
     const uint8_t* base[kLoads];
     uint32_t off[kLoads];
 };
 
 __device__ __forceinline__ void issue_stage(uint8_t* buf, const Loads& ld, int s, int wave) {
-    const int f = first_instr(wave);
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
-        if (q < 4 || wave < 4)
-            __builtin_amdgcn_global_load_lds((const void*)(ld.base[q] + ld.off[q] + (uint32_t)s * kStage),
-                                             (lds_void*)(buf + (f + q) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ld.base[q] + ld.off[q] + (uint32_t)s * kStage),
+                                         (lds_void*)(buf + (kLoads * wave + q) * 1024), 16, 0, 0);
 }
 
 }  // namespace
@@ -99,6 +98,7 @@ __global__ __launch_bounds__(512) void mid_kernel(GArgs A, TileList L) {
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / 4, wn = wave % 4;
 
     for (TileIter it(L, ntn); it.valid(); it.next()) {
         // ---- decode: tiles of a group are n-tile-major, m-tiles innermost
@@ -135,10 +135,9 @@ __global__ __launch_bounds__(512) void mid_kernel(GArgs A, TileList L) {
         {
             const uint8_t* abase = uniform_ptr(PHASE == 0 ? (gi.shared ? A.a_sh : A.a) : A.h);
             const size_t ew = (size_t)gi.e * H * I * 2;   // one expert's matrix, bytes
-            const int f = first_instr(wave);
 #pragma unroll
             for (int q = 0; q < kLoads; ++q) {
-                const int row0 = 8 * min(f + q, kInstr - 1);   // wave-uniform (waves 4-7: q = 4 unused)
+                const int row0 = 8 * (kLoads * wave + q);   // wave-uniform
                 const int row = row0 + lane / 8;
                 const uint32_t c16 = (uint32_t)(((lane % 8) ^ swz_key(row)) * 16);
                 if (row0 < kM) {
@@ -153,74 +152,62 @@ __global__ __launch_bounds__(512) void mid_kernel(GArgs A, TileList L) {
             }
         }
 
-        // 16x16 blocks (v_mfma_f32_16x16x32_bf16): row blocks i (rows 16 i),
-        // column blocks j: gate/up j = 0 gate columns 16 w, j = 1 up columns
-        // 128 + 16 w; down columns 32 w + 16 j
-        f32x4 acc[2][2] = {};
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
         issue_stage(ring, ld, 0, wave);
         issue_stage(ring + kStageBytes, ld, 1, wave);
-        if (2 < nst) issue_stage(ring + 2 * kStageBytes, ld, 2, wave);
-        const int bcol0 = kM + (PHASE == 0 ? 16 * wave : 32 * wave);
-        const int bcol1 = kM + (PHASE == 0 ? 128 + 16 * wave : 32 * wave + 16);
+        // B rows of the wave's blocks: gate/up j = 0 gate rows 32 wn, j = 1 up
+        // rows 128 + 32 wn; down rows 64 wn + 32 j
+        const int brow0 = kM + (PHASE == 0 ? wn * 32 : wn * 64);
+        const int brow1 = kM + (PHASE == 0 ? 128 + wn * 32 : wn * 64 + 32);
+        const int arow = wm * 32 + lane % 32;
         for (int s = 0; s < nst; ++s) {
-            // stage s landed for every wave (this wave's loads of the up to two
-            // later stages, the newest, may still be in flight); the buffer of
-            // stage s-1 is free
-            const int pend = min(nst - 1 - s, 2);
-            if (wave < 4) {
-                if (pend == 2) barrier_vm<2 * kLoads>();
-                else if (pend == 1) barrier_vm<kLoads>();
-                else barrier_vm<0>();
-            } else {
-                if (pend == 2) barrier_vm<2 * (kLoads - 1)>();
-                else if (pend == 1) barrier_vm<kLoads - 1>();
-                else barrier_vm<0>();
-            }
-            if (s + 3 < nst) issue_stage(ring + ((s + 3) % kRing) * kStageBytes, ld, s + 3, wave);
+            // stage s landed for every wave (this wave's stage s+1 loads, the
+            // newest, may still be in flight); the buffer of stage s-1 is free
+            if (s + 1 < nst)
+                barrier_vm<kLoads>();
+            else
+                barrier_vm<0>();
+            if (s + 2 < nst) issue_stage(ring + ((s + 2) % kRing) * kStageBytes, ld, s + 2, wave);
             const uint8_t* cur = ring + (s % kRing) * kStageBytes;
-            // operand: lane l takes row l%16 of the block, bytes [64 ks + 16 (l/16), +16)
-            bf16x8 a[2][2], b[2][2];
-            auto rd = [&](int ks, bf16x8 (&x)[2], bf16x8 (&y)[2]) {
-                const int c = ks * 4 + lane / 16;
-                x[0] = *(const bf16x8*)(cur + swz(lane % 16, c));
-                x[1] = *(const bf16x8*)(cur + swz(16 + lane % 16, c));
-                y[0] = *(const bf16x8*)(cur + swz(bcol0 + lane % 16, c));
-                y[1] = *(const bf16x8*)(cur + swz(bcol1 + lane % 16, c));
-            };
-            rd(0, a[0], b[0]);
-            rd(1, a[1], b[1]);
+            // the next k-step's fragments are read while this one's MFMAs run
+            bf16x8 a[2], b0[2], b1[2];
+            a[0] = frag16(cur, arow, lane, 0);
+            b0[0] = frag16(cur, brow0 + lane % 32, lane, 0);
+            b1[0] = frag16(cur, brow1 + lane % 32, lane, 0);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c = ks & 1, n = c ^ 1;
+                if (ks + 1 < 4) {
+                    a[n] = frag16(cur, arow, lane, ks + 1);
+                    b0[n] = frag16(cur, brow0 + lane % 32, lane, ks + 1);
+                    b1[n] = frag16(cur, brow1 + lane % 32, lane, ks + 1);
+                }
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b0[c], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b1[c], acc[1], 0, 0, 0);
+            }
         }
 
-        // ---- epilogue: element q of block (i, j) is row 16 i + 4 (lane/16) + q,
-        // column lane%16 of the block
+        // ---- epilogue: element v of block j is row 32 wm + 8 (v/4) + 4 (lane/32) + v%4,
+        // column lane%32 of the block
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int v = 0; v < 16; ++v) {
+            const int r = wm * 32 + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
+            const int orow = out_row[r];
+            if (orow < 0) continue;
+            if (PHASE == 0) {
+                ((uint16_t*)A.h)[(size_t)orow * I + n0 + wn * 32 + lane % 32] =
+                    (uint16_t)f32_to_bf16_bits(silu_mul(acc[0][v], acc[1][v]));
+            } else {
+                void* yb = gi.shared ? A.y_sh : A.y;
+                const int ybf = gi.shared ? A.y_sh_bf16 : A.y_bf16;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = 16 * i + 4 * (lane / 16) + q;
-                const int orow = out_row[r];
-                if (orow < 0) continue;
-                if (PHASE == 0) {
-                    ((uint16_t*)A.h)[(size_t)orow * I + n0 + 16 * wave + lane % 16] =
-                        (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][0][q], acc[i][1][q]));
-                } else {
-                    void* yb = gi.shared ? A.y_sh : A.y;
-                    const int ybf = gi.shared ? A.y_sh_bf16 : A.y_bf16;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const size_t o = (size_t)orow * H + n0 + 32 * wave + 16 * j + lane % 16;
-                        if (ybf) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
-                        else ((float*)yb)[o] = acc[i][j][q];
-                    }
+                for (int j = 0; j < 2; ++j) {
+                    const size_t o = (size_t)orow * H + n0 + wn * 64 + 32 * j + lane % 32;
+                    if (ybf) ((uint16_t*)yb)[o] = (uint16_t)f32_to_bf16_bits(acc[j][v]);
+                    else ((float*)yb)[o] = acc[j][v];
                 }
             }
+        }
     }
 }
 
