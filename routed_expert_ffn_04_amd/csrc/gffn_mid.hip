@@ -1,10 +1,11 @@
-// Grouped expert FFN, 64-row tiles for bf16 groups of 17-256 rows.
+// Grouped expert FFN, 64-row tiles for bf16 groups of up to 256 rows.
 //
 // "DeepSeek V3/R1 Inference Efficiency (2)", section 1.b: grouped-GEMM
-// efficiency depends on the rows per group.  A group of a few dozen rows
-// multiplies a full [H, 2I] and [I, H] weight pair, so its cost is streaming
-// those weights; the 256-row tiles of gffn_big.hip spend most of each stage's
-// loads on padding rows and keep only one 32 KiB weight stage in flight.
+// efficiency depends on the rows per group.  A group of a few dozen rows (or,
+// in a decode batch, a few) multiplies a full [H, 2I] and [I, H] weight pair,
+// so its cost is streaming those weights; the 256-row tiles of gffn_big.hip
+// spend most of each stage's loads on padding rows and keep only one 32 KiB
+// weight stage in flight.
 //
 // Tile: 64 rows x 256 MFMA columns (gate/up: 128 gate + 128 up columns of the
 // same 128 h columns; down: 256 output columns), K staged 128 bytes (64 bf16)
