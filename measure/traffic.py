@@ -53,7 +53,8 @@ def build_probe() -> str:
         raise RuntimeError(f"moe_probe build failed:\n{r.stderr}")
     os.replace(PROBE + ".tmp", PROBE)
     return PROBE
-GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::big_kernel", "moe::mx_", "moe::mxbig_kernel", "moe::gffn_build_lists")
+GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::mid_kernel", "moe::big_kernel", "moe::mx_", "moe::mxbig_kernel",
+                "moe::gffn_build_lists")
 XCDS = 8          # MI355X accelerator dies
 NAMES = {
     1: "tiny-fp32-T64-H256-E8-top2",

@@ -12,7 +12,7 @@ fp8 weights (e4m3, MXFP4) rel-Frobenius <= 5e-3 and max-abs <= 2^-6 max|ref|
 1e-3 to 2.4e-3: the outputs are bf16, and the matrix cores' fp8 sums differ
 from fp64 enough to move a few e4m3 codes of h per row and, through them,
 bf16 roundings of the outputs; a dropped 128-wide K block would move a row
-by 1/56 (gate/up) to 1/16 (down) of its norm.
+by about 1/sqrt(56) (gate/up) to 1/sqrt(16) (down) of its norm.
 """
 import os
 import sys
