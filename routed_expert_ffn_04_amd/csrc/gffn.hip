@@ -14,9 +14,10 @@
 //   class 2: otherwise        256 x 256 MFMA tiles (bf16 / e4m3, gffn_big.hip),
 //                             or 64-row LDS tiles (fp32 or H % 256 != 0)
 // (fp32 and e4m3 layers put every group in class 2; MXFP4 layers use the
-// MX weight-streaming tiles of gffn_mx.hip, 16 rows for m <= 16 and 64 up to
-// 256, and the 256 x 256 MX tiles of gffn_mxbig.hip above, with the same
-// promotion of many mid-sized groups as bf16).  One single-workgroup kernel
+// MX weight-streaming tiles of gffn_mx.hip, 16 rows for m <= 32, and the
+// 256 x 256 MX tiles of gffn_mxbig.hip above; groups of 33-256 rows join the
+// 16-row tiles when there are at most four of them, else the large tiles,
+// and take 64-row streaming tiles only where the large tiles do not apply).  One single-workgroup kernel
 // writes, per class, the list of (group, first row) m-tiles with the heaviest
 // groups first (longest-processing-time order); then each class's gate/up
 // kernel and down kernel run as persistent grids that walk their list (see
@@ -209,12 +210,13 @@ static bool use_mxbig(int H, int I, int R_max, int S) {
            (uint64_t)H * I / 2 < lim;
 }
 
-constexpr int kPromoteMin = 32;
 constexpr int kDemoteMax = 4;
 
 // MXFP4: groups of up to this many rows take the 16-row streaming tiles
-// (several m-tiles of one group re-read its weights, mostly from L2).
-constexpr int kMxC0Max = 16;
+// (several m-tiles of one group re-read its weights, mostly from L2).  With
+// 256 groups, 24 and 32 rows ran 16% and 13% faster there than on the
+// 256 x 256 MX tiles; 48 and 64 rows 24% and 60% slower.
+constexpr int kMxC0Max = 32;
 
 static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
     ClassSpec c{};
@@ -225,7 +227,11 @@ static ClassSpec class_spec(int dt, int H, int I, int R_max, int S) {
         c.mlo[1] = kMxC0Max; c.mhi[1] = big ? 256 : 1 << 30;  c.bm[1] = 64;
         c.mlo[2] = 256; c.mhi[2] = big ? 1 << 30 : 0;  c.bm[2] = 256;
         c.demote_max = kDemoteMax;
-        c.promote_min = big ? kPromoteMin : 0;
+        // with the large MX tiles, the middle class never keeps its groups: up
+        // to kDemoteMax of them join the 16-row tiles, more join the large
+        // tiles (16 groups of 65-256 rows: 2-3x faster there than on the
+        // 64-row streaming tiles), so its launches are skipped
+        c.promote_min = big ? kDemoteMax + 1 : 0;
     } else if (dt == DT_BF16) {
         // with the large tiles available (H % 256 == 0, 32-bit offsets), every
         // group of up to 256 rows takes the 64-row ring tiles, which share
@@ -306,15 +312,17 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
         dn[k] = TileList{lo.entries[k], lo.counts + k};
     }
     // phase 1 (all classes), then phase 2: a group's down tiles need all of its h
+    // the middle class always moves its groups out (demoted or promoted)
+    const bool c1_empty = cs.promote_min > 0 && cs.promote_min == cs.demote_max + 1;
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
-        if (me[k] == 0) continue;
+        if (me[k] == 0 || (k == 1 && c1_empty)) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_gateup(A, up[k], s) : launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s))
           : k == 1 && cs.mid1 ? launch_mid_gateup(A, up[k], s)
           : k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
                   : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
-        if (me[k] == 0) continue;
+        if (me[k] == 0 || (k == 1 && c1_empty)) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_down(A, dn[k], s) : launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s))
           : k == 1 && cs.mid1 ? launch_mid_down(A, dn[k], s)
           : k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)

@@ -60,12 +60,14 @@ GROUPED_CASES = [
     # group rows (0 = empty expert), shared rows, H, I
     ([130, 5, 0, 64, 1], 40, 256, 256),        # 16-row and 64-row tiles, a ragged 130
     ([3, 77, 200], 0, 384, 512),               # odd number of 128-wide k-steps (no K split)
-    ([16, 17, 2], 33, 512, 384),               # class boundaries; odd k-steps in the down projection
+    ([32, 33, 2], 17, 512, 384),               # class boundaries; odd k-steps in the down projection
     ([9, 40, 3], 20, 1280, 1152),              # full rings of loads in flight plus tails, both projections
     ([5, 30, 2], 18, 4352, 2176),              # exponents in 16-step blocks (2 blocks + 2 / 1 block + 1 tail steps)
-    # more than a handful of 17..256-row groups: they keep the 64-row tiles
+    # five or more groups of 33..256 rows: promoted to the 256-row MX tiles
     # (up to four such groups are cut into 16-row tiles instead)
     ([20, 33, 50, 70, 100, 5, 250], 17, 512, 256),
+    # H % 256 != 0 (no large MX tiles): groups of 33..256 rows on the 64-row streaming tiles
+    ([40, 90, 33, 250, 170, 60], 0, 384, 256),
     # 256 x 256 MX tiles: exact, partial (one row over) and multi m-tiles, a large shared group
     ([300, 600, 257, 20, 512], 280, 512, 256),
     # a 16-stage K ring (three stages rotating) in gate/up, partial tiles
