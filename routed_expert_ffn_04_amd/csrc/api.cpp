@@ -343,6 +343,7 @@ moe_status_t moe_layer(const void* x, int32_t x_dt, int32_t T, int32_t H, const 
         p.dt = wdt; p.a = a; p.a_scale = as; p.src = src; p.src_div = k;
         p.offsets = offsets; p.G = E; p.R_max = R; p.routed = to_bank(routed);
         p.a_sh = a; p.a_sh_scale = as; p.S = has_sh ? T : 0; p.has_shared = has_sh; p.shared = to_bank(shared);
+        p.m_max = T;   // the router picks k distinct experts per token
         p.H = H; p.I = I; p.y = w8 + L.yperm; p.y_sh = has_sh ? w8 + L.ysh : nullptr;
         p.y_bf16 = y_dt == MOE_BF16; p.y_e4m3 = y_dt == MOE_E4M3; p.y_scale = (float*)(w8 + L.yscale);
         p.y_sh_bf16 = ybf;

@@ -314,15 +314,24 @@ hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s) {
     // phase 1 (all classes), then phase 2: a group's down tiles need all of its h
     // the middle class always moves its groups out (demoted or promoted)
     const bool c1_empty = cs.promote_min > 0 && cs.promote_min == cs.demote_max + 1;
+    // classes no group can reach under the caller's row bound are not launched
+    // (their lists stay empty: a group lands only in a class whose range or
+    // whose promotion source range it reaches)
+    bool reach[kClasses];
+    for (int k = 0; k < kClasses; ++k) {
+        const bool own = p.m_max <= 0 || p.m_max > cs.mlo[k];
+        const bool promoted = k == 2 && cs.promote_min > 0 && (p.m_max <= 0 || p.m_max > cs.mlo[1]);
+        reach[k] = own || promoted;
+    }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
-        if (me[k] == 0 || (k == 1 && c1_empty)) continue;
+        if (me[k] == 0 || (k == 1 && c1_empty) || !reach[k]) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_gateup(A, up[k], s) : launch_mx_gateup(k == 0 ? 1 : 4, A, up[k], s))
           : k == 1 && cs.mid1 ? launch_mid_gateup(A, up[k], s)
           : k < 2 ? launch_stream_gateup(k == 0 ? 1 : 4, A, up[k], s)
                   : cs.bm[k] == 256 ? launch_big_gateup(p.dt, A, up[k], s) : launch_tile_gateup(p.dt, A, up[k], cs.bm[k], s);
     }
     for (int k = 0; k < kClasses && e == hipSuccess; ++k) {
-        if (me[k] == 0 || (k == 1 && c1_empty)) continue;
+        if (me[k] == 0 || (k == 1 && c1_empty) || !reach[k]) continue;
         e = p.dt == DT_MXFP4 ? (k == 2 ? launch_mxbig_down(A, dn[k], s) : launch_mx_down(k == 0 ? 1 : 4, A, dn[k], s))
           : k == 1 && cs.mid1 ? launch_mid_down(A, dn[k], s)
           : k < 2 ? launch_stream_down(k == 0 ? 1 : 4, A, dn[k], s)

@@ -52,6 +52,11 @@ struct GffnProblem {
     void* y; void* y_sh; int y_bf16;   // routed outputs bf16 (else fp32 unless y_e4m3)
     int y_e4m3; float* y_scale;        // routed outputs as e4m3 + [R_max][H/128] scales
     int y_sh_bf16;                     // shared outputs bf16 (else fp32)
+    // An upper bound on the rows of any group (routed or shared) that the
+    // caller guarantees, 0 if none: tile classes no group can reach are then
+    // not launched.  The fused layer knows it (T: a token picks an expert at
+    // most once); the grouped call alone does not.
+    int m_max;
 };
 
 size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt);
