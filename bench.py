@@ -1,12 +1,15 @@
 """Benchmark of the MI355X sparse MoE FFN layer (one GPU).
 
 One step = one pass of the whole hot path over one batch of synthetic tokens:
-route -> (fp8 layers: quantise x) -> permute -> grouped FFN -> combine, each
-through the library's C ABI on torch's current stream (the same kernels
-moe_layer enqueues).  Inputs are resident in HBM before the timed region.
-HIP events around each call inside the timed region give per-call times; the
-grouped FFN (tile builder + gate/up kernel + down kernel) is the dominant call
-and its roofline fraction is reported against the MI355X peaks.
+route -> (fp8 layers: quantise x) -> permute -> grouped FFN -> combine.  Inputs
+are resident in HBM before the timed regions.  Each layer workload is timed
+twice on torch's current stream, for the same number of steps:
+  * the five C-ABI calls, with HIP events around each call: per-call times;
+    the grouped FFN (tile builder + gate/up kernel + down kernel) is the
+    dominant call and its roofline fraction comes from its events;
+  * the fused moe_layer call (the same kernels, enqueued back to back by the
+    library), with one event pair around the timed steps: `value` and
+    `ms_per_step`.  Its output is checked bit for bit against the five calls'.
 
 Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped decode batch
 (T = 128, H = 7168, 256 routed experts + 1 shared, I = 2048, top-8, bf16),
@@ -157,6 +160,29 @@ class LayerRunner:
         yield "combine", lambda: moe.combine(self.y, self.y_sh, self.dest, self.w, out=self.out, y_scale=self.y_scale)
 
 
+class FusedRunner:
+    """The layer as one moe_layer call: the library enqueues route, quantise,
+    permute, grouped FFN and combine back to back on the stream, with the
+    same kernels (and the same operand buffers' layout) as the five calls."""
+
+    def __init__(self, lr: LayerRunner, dev):
+        wl = self.wl = lr.wl
+        self.lr = lr
+        self.y_dtype = torch.uint8 if lr.fp8_combine else None
+        rs = lr.routed.struct()
+        y_dt = moe.E4M3 if lr.fp8_combine else moe._dt_of(lr.out)
+        need = moe.layer_workspace_size(wl.T, wl.H, wl.E, wl.k, wl.I, moe._dt_of(wl.x), rs.dt, lr.shared is not None,
+                                        moe._dt_of(lr.out), y_dt)
+        self.ws = moe._workspace(need, dev)
+        self.out = torch.empty_like(lr.out)
+        self.names = ["layer"]
+
+    def calls(self):
+        wl, lr = self.wl, self.lr
+        yield "layer", lambda: moe.layer(wl.x, wl.w_router, wl.bias, wl.k, wl.score, lr.routed, lr.shared,
+                                         out=self.out, ws=self.ws, y_dtype=self.y_dtype)
+
+
 class GroupedRunner:
     """The pre-routed expert-parallel share: the grouped FFN call alone."""
 
@@ -229,6 +255,28 @@ class ClockSampler:
         s = sorted(self.samples)
         return {"source": self.path, "samples": len(s), "min_mhz": s[0], "median_mhz": s[len(s) // 2],
                 "max_mhz": s[-1]}
+
+
+def run_steps(runner, steps: int, warmup: int):
+    """Mean ms per step over `steps` steps after `warmup`, with one event
+    pair around the whole timed region (nothing recorded between calls)."""
+    for _ in range(warmup):
+        for _, f in runner.calls():
+            f()
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            for _, f in runner.calls():
+                f()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    runner.clock = clk.summary()
+    return start.elapsed_time(end) / steps, wall
 
 
 def run_timed(runner, steps: int, warmup: int):
@@ -366,6 +414,8 @@ def main():
         "roofline": m["roofline"], "grouped_ffn": m["grouped_ffn"], "calls_ms": m["calls_ms"],
         "gpu_clock": m["gpu_clock"],
     }
+    if "timing" in m:
+        res["timing"] = m["timing"]
     if "grouped_ffn_scrubbed" in m:
         res["grouped_ffn_scrubbed"] = m["grouped_ffn_scrubbed"]
     if not args.no_cpu:
@@ -379,7 +429,7 @@ def main():
         p = measure(5, args.prefill_steps, args.warmup, dev)
         p.pop("wl"), p.pop("runner")
         res["prefill_T16384"] = {k: p[k] for k in ("config", "dtype", "value", "unit", "ms_per_step", "roofline",
-                                                   "grouped_ffn", "calls_ms", "gpu_clock")}
+                                                   "grouped_ffn", "calls_ms", "timing", "gpu_clock")}
         res["prefill_T16384"]["steps"] = args.prefill_steps
     print(json.dumps(res), flush=True)
 
@@ -395,8 +445,19 @@ def measure(cid: int, steps: int, warmup: int, dev, mxfp4: bool = False, fp8_com
         wl.y_dt = "e4m3"          # also what the CPU oracle baseline computes
     runner = GroupedRunner(wl, dev) if cid == 4 else LayerRunner(wl, dev, fp8_combine=fp8_combine)
     ms, per, wall = run_timed(runner, steps, warmup)
-    log(f"config {cid}: timed {steps} steps: {ms:.3f} ms/step; per call (ms): " +
+    log(f"config {cid}: five calls, timed {steps} steps: {ms:.3f} ms/step; per call (ms): " +
         ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    calls_ms, clock, fused_same = ms, runner.clock, None
+    if cid != 4:
+        # the headline: the fused layer (one moe_layer call per step), with no
+        # events between its kernels; its output must equal the five calls' bit for bit
+        fused = FusedRunner(runner, dev)
+        ms, wall = run_steps(fused, steps, warmup)
+        clock = fused.clock
+        fused_same = bool(torch.equal(fused.out, runner.out))
+        log(f"config {cid}: fused layer, timed {steps} steps: {ms:.3f} ms/step; output equals the five calls': "
+            f"{fused_same}")
+        del fused
 
     # algorithmic work of the grouped FFN
     if cid == 4:
@@ -449,9 +510,15 @@ def measure(cid: int, steps: int, warmup: int, dev, mxfp4: bool = False, fp8_com
         "config": cfg, "roofline": roof,
         "grouped_ffn": {"ms": round(gffn_ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)},
         "calls_ms": {k: round(v, 4) for k, v in per.items()},
-        "gpu_clock": getattr(runner, "clock", None),
+        "gpu_clock": clock,
         "wl": wl, "runner": runner,
     }
+    if cid != 4:
+        res["timing"] = {"value": "fused moe_layer call per step, one event pair around the timed steps",
+                         "five_calls_ms_per_step": round(calls_ms, 4),
+                         "five_calls": "route, quantise, permute, grouped FFN, combine as separate C-ABI calls, "
+                                       "an event pair around each (calls_ms and the roofline come from these)",
+                         "fused_equals_five_calls": fused_same}
     if cid in (1, 4):
         # small working sets: also the call with caches scrubbed before each repetition
         sms = scrubbed_ms(runner, steps, dev)

@@ -1,6 +1,7 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration
-the benchmark times (the layer as its C-ABI calls, bench.LayerRunner /
-GroupedRunner).
+"""GPU parity at the five workloads' full sizes, in the launch configurations
+the benchmark times: the layer as its C-ABI calls (bench.LayerRunner /
+GroupedRunner), and the fused moe_layer call (bench.FusedRunner), whose output
+must equal the five calls' bit for bit.
 
 Routing (expert ids) and the permutation (counts, offsets, src, dest) are
 compared bit-exactly over every token against the oracle; routing weights
@@ -52,7 +53,9 @@ def _sample(T, n, seed):
 
 def _layer_run_and_routing(cid, fp8c, mxfp4):
     """The layer through bench.LayerRunner at full size; routing and the
-    permutation checked bit-exactly over every token.  Returns (wl, run)."""
+    permutation checked bit-exactly over every token, and the fused layer
+    (bench.FusedRunner) checked to give the same output bits.  Returns
+    (wl, run)."""
     print(f"config {cid}{' with the fp8 combine' if fp8c else ''}{' with MXFP4 weights' if mxfp4 else ''}: generating",
           flush=True)
     wl = synth.config_mxfp4(cid, device=DEV) if mxfp4 else synth.config(cid, device=DEV)
@@ -72,6 +75,12 @@ def _layer_run_and_routing(cid, fp8c, mxfp4):
     np.testing.assert_array_equal(run.offsets.cpu().numpy(), offsets)
     np.testing.assert_array_equal(run.src.cpu().numpy(), src)
     np.testing.assert_array_equal(run.dest.cpu().numpy(), dest)
+    fused = bench.FusedRunner(run, DEV)
+    for _, f in fused.calls():
+        f()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.out, run.out), "fused layer differs from the five calls"
+    del fused
     return wl, run
 
 
