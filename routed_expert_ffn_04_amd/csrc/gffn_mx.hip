@@ -19,10 +19,13 @@
 //                    (bytes 16-31);
 //   E8M0 exponents:  the block of K 32g .. 32g+31 of both operands.
 // The weight operand is 16 contiguous bytes of an output-major weight row and
-// the activation operand two 16-byte pieces of a row, so both are read from
-// memory straight into registers (the weight never touches LDS); the
+// the activation operand two 16-byte pieces of a row, so both can be read
+// from memory straight into registers (the weight never touches LDS); the
 // exponents of a step's four K blocks are one dword, from which each lane
-// shifts out its own byte.
+// shifts out its own byte.  The 16-row gate/up tiles instead bring the
+// tile's activation rows and their exponents into LDS once per tile with
+// direct loads (all four waves read the same rows at every step, which as
+// register loads cost more than the weights' own share of the load path).
 //
 // Like the bf16 streaming kernels (gffn_stream.hip): tiles of MB*16 rows x TN
 // columns x all of K, P k-steps of loads in flight per wave, waves split K
@@ -85,8 +88,10 @@ __device__ __forceinline__ long act_row(const GArgs& A, const GroupInfo& gi, int
 }  // namespace
 
 // ---------------------------------------------------------------- gate / up
-template <int MB, int KS, int P, int kNB, bool XEX>
+template <int MB, int KS, int P, int kNB, bool XEX, bool LDSA = false>
 __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
+    static_assert(!LDSA || (MB == 1 && KS == 1 && !XEX), "activations in LDS: 16-row tiles, all of K per wave, "
+                                                         "exponent dwords per step");
     constexpr int NW = 4 / KS;                 // waves along N
     constexpr int TN = NW * kNB * 16;          // h columns per tile (a multiple of 32)
     constexpr int RS = 2 * TN + 1;
@@ -95,6 +100,12 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     const int nsteps = H / 128 / KS;           // k-steps of 128 per wave
 
     __shared__ float red[KS][16 * MB][RS];
+    // LDSA: the tile's 16 activation rows [16][H + 16] (codes; the 16 spare
+    // bytes per row spread the rows over the LDS banks), then their exponent
+    // rows [16][H/32 + 4]
+    extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
+    const int astride = H + 16, estride = H / 32 + 4;
+    const uint8_t* exp_lds = act_lds + 16 * astride;
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int kw = wave % KS, nw = wave / KS;
@@ -116,6 +127,29 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
 
         const uint8_t* abase = gi.shared ? A.a_sh : A.a;
         const uint8_t* aebase = (const uint8_t*)(gi.shared ? A.a_sh_scale : A.a_scale);
+        if constexpr (LDSA) {
+            // the tile's rows (rows past the group's end: its last row) by
+            // direct loads, wave w rows 4w..4w+3, once per tile
+#pragma unroll 1
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 4 * wave + rr;
+                const long ar = act_row(A, gi, min(m0 + row, gi.m - 1));
+                const uint8_t* src = abase + (size_t)ar * H;
+                const uint8_t* esrc = aebase + (size_t)ar * (H / 32);
+                uint8_t* dst = act_lds + row * astride;
+                uint8_t* edst = (uint8_t*)exp_lds + row * estride;
+                for (int c = 0; c < H; c += 1024)
+                    if (c + lane * 16 < H)
+                        __builtin_amdgcn_global_load_lds((const void*)(src + c + lane * 16),
+                                                         (__attribute__((address_space(3))) void*)(dst + c), 16, 0, 0);
+                for (int c = 0; c < H / 32; c += 256)
+                    if (c + lane * 4 < H / 32)
+                        __builtin_amdgcn_global_load_lds((const void*)(esrc + c + lane * 4),
+                                                         (__attribute__((address_space(3))) void*)(edst + c), 4, 0, 0);
+            }
+            wait_vm<0>();
+            __syncthreads();
+        }
         const uint8_t* ap[MB];
         const uint8_t* aep[MB];
 #pragma unroll
@@ -152,8 +186,10 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                 rg[p][c] = gld<i32x4>(gp[c] + step * 64);
                 ru[p][c] = gld<i32x4>(up[c] + step * 64);
             }
+            if constexpr (!LDSA) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) ra[p][i] = load_act(ap[i] + step * 128);
+                for (int i = 0; i < MB; ++i) ra[p][i] = load_act(ap[i] + step * 128);
+            }
         };
         auto load_e = [&](int p, int step) {
 #pragma unroll
@@ -161,8 +197,10 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                 rge[p][c] = gld<uint32_t>(gep[c] + step * 4);
                 rue[p][c] = gld<uint32_t>(uep[c] + step * 4);
             }
+            if constexpr (!LDSA) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
+                for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
+            }
         };
         auto load_x = [&](int blk, i32x4 (&xg)[kNB], i32x4 (&xu)[kNB], i32x4 (&xa)[MB]) {
 #pragma unroll
@@ -170,8 +208,10 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                 xg[c] = gld<i32x4>(gep[c] + blk * 64 + kq * 16);
                 xu[c] = gld<i32x4>(uep[c] + blk * 64 + kq * 16);
             }
+            if constexpr (!LDSA) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) xa[i] = gld<i32x4>(aep[i] + blk * 64 + kq * 16);
+                for (int i = 0; i < MB; ++i) xa[i] = gld<i32x4>(aep[i] + blk * 64 + kq * 16);
+            }
         };
         auto next_block = [&]() {
 #pragma unroll
@@ -179,12 +219,24 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                 xcg[c] = xng[c];
                 xcu[c] = xnu[c];
             }
+            if constexpr (!LDSA) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) xca[i] = xna[i];
+                for (int i = 0; i < MB; ++i) xca[i] = xna[i];
+            }
         };
         // step p of the ring; s0 (a multiple of 4 when XE) is the ring's first step
         auto mma = [&](int p, int s0, bool x) {
             uint32_t ea[MB], eg[kNB], eu[kNB];
+            i32x8 av[MB];
+            if constexpr (LDSA) {
+                // lane group kq: bytes 16 kq .. +15 and 64 + 16 kq .. +15 of the step's 128
+                const uint8_t* q = act_lds + (lane % 16) * astride + (s0 + p) * 128 + kq * 16;
+                const i32x4 lo = *(const i32x4*)q, hi = *(const i32x4*)(q + 64);
+                av[0] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            } else {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) av[i] = ra[p][i];
+            }
             if (x) {
                 const int src = (lane & 15) + 16 * (((s0 + p) & 15) >> 2);
 #pragma unroll
@@ -192,23 +244,28 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                     eg[c] = xlane(src, xcg[c][p & 3]) >> esh;
                     eu[c] = xlane(src, xcu[c][p & 3]) >> esh;
                 }
+                if constexpr (!LDSA) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
+                    for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
+                }
             } else {
 #pragma unroll
                 for (int c = 0; c < kNB; ++c) {
                     eg[c] = rge[p][c] >> esh;
                     eu[c] = rue[p][c] >> esh;
                 }
+                if constexpr (!LDSA) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
+                    for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
+                }
             }
+            if constexpr (LDSA) ea[0] = *(const uint32_t*)(exp_lds + (lane % 16) * estride + (s0 + p) * 4) >> esh;
 #pragma unroll
             for (int c = 0; c < kNB; ++c)
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    accg[i][c] = mma_f8f4(ra[p][i], rg[p][c], accg[i][c], ea[i], eg[c]);
-                    accu[i][c] = mma_f8f4(ra[p][i], ru[p][c], accu[i][c], ea[i], eu[c]);
+                    accg[i][c] = mma_f8f4(av[i], rg[p][c], accg[i][c], ea[i], eg[c]);
+                    accu[i][c] = mma_f8f4(av[i], ru[p][c], accu[i][c], ea[i], eu[c]);
                 }
         };
         // ring of P k-steps in flight over the largest multiple of P (of 16
@@ -478,6 +535,11 @@ static int mx_persistent_grid(K kernel) {
 constexpr int kMxGuKs = 1, kMxGuP = 8, kMxGuNb = 2;
 constexpr bool kMxGuXe = false;
 constexpr int kMxDnP = 4, kMxDnNb = 4;
+// 16-row gate/up tiles stage the tile's activation rows and exponents in LDS
+// where they fit beside the 16 KiB partial-sum table (H up to 8192): decode
+// layer T = 128 gate/up 0.77 -> 0.74 ms.  Exponent dwords per step there: the
+// 16-step exponent blocks were slower (0.85 ms).
+constexpr size_t kMxGuLdsMax = 140 * 1024;
 constexpr bool kMxDnXe = true;
 // 16-row tiles.  gate/up: K split over kMxGuKs waves when the 128-wide
 // k-steps divide evenly, kMxGuNb column blocks per wave when I is a
@@ -491,6 +553,17 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
     constexpr int KS = kMxGuKs, NB = kMxGuNb;
     constexpr bool XE = kMxGuXe;
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
+    const size_t alds = (size_t)16 * (A.H + 16) + (size_t)16 * (A.H / 32 + 4);
+    if (mb == 1 && alds <= kMxGuLdsMax && A.I % (4 * NB * 16) == 0) {
+        auto k = mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
+        static DeviceCache cache;
+        const int g = per_device(cache, [k] {
+            (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGuLdsMax);
+            return device_cu_count();   // one workgroup per CU (LDS)
+        });
+        hipLaunchKernelGGL(k, dim3(g), dim3(256), alds, s, A, L);
+        return hipGetLastError();
+    }
     if (mb == 1) {
         if (nst % KS == 0 && A.I % (4 / KS * NB * 16) == 0) MOE_MX_LAUNCH((mx_gateup_kernel<1, KS, kMxGuP, NB, XE>));
         else MOE_MX_LAUNCH((mx_gateup_kernel<1, 1, kMxGuP, 2, XE>));
