@@ -139,14 +139,20 @@ __global__ __launch_bounds__(1024) void gffn_build_lists(const int32_t* __restri
                               (unsigned long long)i;
     }
     __syncthreads();
-    // ascending bitonic sort: thread t compares slot i (bit j of i clear) with i + j
-    for (int k = 2; k <= kSortSlots; k <<= 1)
+    // ascending bitonic sort of the first n2 slots (the smallest power of two
+    // >= ng; the slots past ng hold ~0 and stay last): thread t < n2/2
+    // compares slot i (bit j of i clear) with i + j
+    int n2 = 2;
+    while (n2 < ng) n2 <<= 1;
+    for (int k = 2; k <= n2; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1));
-            const unsigned long long a = keys[i], b = keys[i + j];
-            if ((a > b) == ((i & k) == 0)) {
-                keys[i] = b;
-                keys[i + j] = a;
+            if (tid < n2 / 2) {
+                const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1));
+                const unsigned long long a = keys[i], b = keys[i + j];
+                if ((a > b) == ((i & k) == 0)) {
+                    keys[i] = b;
+                    keys[i + j] = a;
+                }
             }
             __syncthreads();
         }

@@ -12,6 +12,10 @@
 //      expert; rank = popcount of lower peers) plus the counts of the lower
 //      waves of the chunk, and scatters src/dest.
 // Sizes: chunk = 1024 items (16 waves); E <= 1024.
+// Up to kSmallChunks chunks (a decode batch: T*k = 1024 at T = 128, k = 8)
+// one workgroup does all three steps in one launch, taking the chunks in
+// order with running per-expert bases: the same positions, without the two
+// extra launches.
 #include "common.h"
 #include "internal.h"
 
@@ -19,6 +23,7 @@ namespace moe {
 
 constexpr int kChunk = 1024;
 constexpr int kChunkWaves = kChunk / kWave;
+constexpr int kSmallChunks = 2;
 
 static inline int nchunks(int R) { return (R + kChunk - 1) / kChunk; }
 
@@ -105,19 +110,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     }
 }
 
-__global__ __launch_bounds__(kChunk) void perm_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                              int nbits, const int32_t* __restrict__ chunk_base,
-                                                              int32_t* __restrict__ src, int32_t* __restrict__ dest) {
-    __shared__ int32_t wcnt[kChunkWaves][1024];   // items of expert e in wave w
+// Ranks of the items of one chunk (flat indices c0 .. c0+1023) within their
+// expert: wave64 multisplit on the id bits; wcnt[w][e] receives the number
+// of items of expert e in wave w.  Returns the rank among the wave's items of
+// the same expert, or -1 for an item past R or with an out-of-range id.
+__device__ __forceinline__ int chunk_rank(const int32_t* __restrict__ ids, int R, int E, int nbits, int c0,
+                                          int32_t (*wcnt)[1024], int& e_out) {
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const int f = blockIdx.x * kChunk + tid;
+    const int f = c0 + tid;
     const int e0 = f < R ? ids[f] : -1;
     const bool valid = (unsigned)e0 < (unsigned)E;        // out-of-range ids are dropped
     const int e = valid ? e0 : 0;
-    // zero only the entries this chunk will read
-    for (int i = tid; i < kChunkWaves * E; i += kChunk) wcnt[i / E][i % E] = 0;
-    __syncthreads();
-    // multisplit: lanes of this wave holding the same expert
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
         const uint64_t m = __ballot(valid && ((e >> b) & 1));
@@ -125,14 +128,81 @@ __global__ __launch_bounds__(kChunk) void perm_scatter_kernel(const int32_t* __r
     }
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const int rank = __popcll(peers & lower);
-    const bool leader = valid && ((peers & lower) == 0);
-    if (leader) wcnt[w][e] = __popcll(peers);
+    if (valid && (peers & lower) == 0) wcnt[w][e] = __popcll(peers);
+    e_out = e;
+    return valid ? rank : -1;
+}
+
+__global__ __launch_bounds__(kChunk) void perm_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                              int nbits, const int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ src, int32_t* __restrict__ dest) {
+    __shared__ int32_t wcnt[kChunkWaves][1024];   // items of expert e in wave w
+    const int tid = threadIdx.x, w = tid / kWave;
+    const int f = blockIdx.x * kChunk + tid;
+    // zero only the entries this chunk will read
+    for (int i = tid; i < kChunkWaves * E; i += kChunk) wcnt[i / E][i % E] = 0;
     __syncthreads();
-    if (valid) {
+    int e;
+    const int rank = chunk_rank(ids, R, E, nbits, blockIdx.x * kChunk, wcnt, e);
+    __syncthreads();
+    if (rank >= 0) {
         int pos = chunk_base[(size_t)blockIdx.x * E + e] + rank;
         for (int i = 0; i < w; ++i) pos += wcnt[i][e];
         src[pos] = f;
         dest[f] = pos;
+    }
+}
+
+__global__ __launch_bounds__(kChunk) void perm_small_kernel(const int32_t* __restrict__ ids, int R, int E, int nbits,
+                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ src, int32_t* __restrict__ dest) {
+    __shared__ int32_t wcnt[kChunkWaves][1024];   // items of expert e in wave w of the current chunk
+    __shared__ int32_t base[1024];                // per expert: count, then next free position
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    base[tid] = 0;
+    __syncthreads();
+    for (int f = tid; f < R; f += kChunk) {
+        const int e = ids[f];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&base[e], 1);   // counts only: order-free
+    }
+    __syncthreads();
+    // exclusive scan over experts (1024 entries, one per thread; entries >= E are 0)
+    const int32_t c = base[tid];
+    int32_t v = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    if (lane == kWave - 1) wsum[w] = v;
+    __syncthreads();
+    int32_t wb = 0;
+    for (int i = 0; i < w; ++i) wb += wsum[i];
+    base[tid] = wb + v - c;
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = wb + v - c;
+    }
+    if (tid == 0) offsets[E] = R;
+    for (int c0 = 0; c0 < R; c0 += kChunk) {
+        for (int i = tid; i < kChunkWaves * E; i += kChunk) wcnt[i / E][i % E] = 0;
+        __syncthreads();   // also: the bases of the previous chunk are in place
+        int e;
+        const int rank = chunk_rank(ids, R, E, nbits, c0, wcnt, e);
+        __syncthreads();
+        if (rank >= 0) {
+            int pos = base[e] + rank;
+            for (int i = 0; i < w; ++i) pos += wcnt[i][e];
+            src[pos] = c0 + tid;
+            dest[c0 + tid] = pos;
+        }
+        __syncthreads();
+        for (int e2 = tid; e2 < E; e2 += kChunk) {
+            int32_t n = 0;
+            for (int i = 0; i < kChunkWaves; ++i) n += wcnt[i][e2];
+            base[e2] += n;
+        }
     }
 }
 
@@ -142,6 +212,11 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int
     int32_t* chunk = (int32_t*)ws;
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
+    if (nch <= kSmallChunks) {
+        hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(kChunk), 0, s, ids, R, E, nbits, counts, offsets, src,
+                           dest);
+        return hipGetLastError();
+    }
     if (nch > 0) {
         hipLaunchKernelGGL(perm_hist_kernel, dim3(nch), dim3(kChunk), 0, s, ids, R, E, chunk);
     }

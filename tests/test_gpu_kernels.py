@@ -113,6 +113,10 @@ PERMUTE_CASES = [
     ("uniform", 1, 1, 1),
     ("uniform", 777, 3, 1024),      # E at the maximum
     ("uniform", 16384, 8, 256),
+    # one-workgroup path (at most two chunks): E at the maximum, ragged second chunk, skew
+    ("uniform", 256, 8, 1024),
+    ("onehot", 200, 8, 256),
+    ("skew", 100, 6, 300),
 ]
 
 
