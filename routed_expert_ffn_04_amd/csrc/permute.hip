@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kChunk) void perm_small_kernel(const int32_t* __res
     if (tid == 0) offsets[E] = R;
     for (int c0 = 0; c0 < R; c0 += kChunk) {
         for (int i = tid; i < kChunkWaves * E; i += kChunk) wcnt[i / E][i % E] = 0;
-        __syncthreads();   // also: the bases of the previous chunk are in place
+        __syncthreads();
         int e;
         const int rank = chunk_rank(ids, R, E, nbits, c0, wcnt, e);
         __syncthreads();
@@ -203,6 +203,7 @@ __global__ __launch_bounds__(kChunk) void perm_small_kernel(const int32_t* __res
             for (int i = 0; i < kChunkWaves; ++i) n += wcnt[i][e2];
             base[e2] += n;
         }
+        __syncthreads();   // the counts are read before the next chunk clears them
     }
 }
 
