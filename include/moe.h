@@ -91,6 +91,12 @@ typedef struct {
     const void* s_gate;         /* E4M3: fp32 [n][I/128][H/128]; MXFP4: uint8 [n][I][H/32] */
     const void* s_up;           /* E4M3: fp32 [n][I/128][H/128]; MXFP4: uint8 [n][I][H/32] */
     const void* s_down;         /* E4M3: fp32 [n][H/128][I/128]; MXFP4: uint8 [n][H][I/32] */
+    /* MXFP4 only, optional (NULL: unused; s_* stay required): the same
+     * exponents in the order the 16-row MXFP4 streaming tiles read them,
+     * written by moe_mx_pack_scales.  Used when the routed bank and (if
+     * present) the shared bank both carry them. */
+    const void* s_gate_up_packed;   /* uint8 [n][I/32][H/512][64][16] */
+    const void* s_down_packed;      /* uint8 [n][H/64][I/512][64][16] */
 } moe_experts_t;
 
 /* ---- routing ("How DeepSeek inference works", "What does DeepSeek inference
@@ -194,6 +200,27 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale,
                              void* ws, size_t ws_bytes, void* stream);
 size_t moe_grouped_ffn_workspace_size(int32_t R_max, int32_t G, int32_t S, int32_t H,
                                       int32_t I, int32_t w_dt);
+
+/* ---- packed MXFP4 exponents (for MXFP4 expert weights, the FP4 MoE GEMMs
+ * of "How DeepSeek inference works", deployment lever table) --------------
+ * A weight-load-time step, not part of the per-token path: writes the E8M0
+ * exponents of an MXFP4 bank (s_gate, s_up [n][I][H/32], s_down [n][H][I/32])
+ * again, permuted into the order in which the 16-row MXFP4 streaming tiles
+ * consume them, so that one 16-byte load per lane brings exactly the
+ * exponents the lane needs for four 128-wide k-steps of four weight blocks.
+ * With c = lane / 16 (32-wide K block within a step), r = lane % 16 (row in
+ * a 16-row weight block), q = 4 ss + b (ss: step within the group of four,
+ * b: block):
+ *   s_gate_up_packed[e][i32][j][lane][q] = (b < 2 ? s_gate : s_up)
+ *       [e][32 i32 + 16 (b % 2) + r][4 (4 j + ss) + c]
+ *   s_down_packed[e][h64][j][lane][q] = s_down[e][64 h64 + 16 b + r][4 (4 j + ss) + c]
+ * Sizes: 2 n I (H/32) and n H (I/32) bytes, 16-byte aligned, owned by the
+ * caller.  Requires dt == MOE_MXFP4 with H % 1024 == 0 and I % 512 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise); a bank is not modified.  Either output
+ * may be NULL (not written).  Enqueued on `stream`.  A bank carrying the
+ * packed exponents gives results identical to the same bank without them. */
+moe_status_t moe_mx_pack_scales(const moe_experts_t* bank, void* s_gate_up_packed, void* s_down_packed,
+                                void* stream);
 
 /* ---- combine ------------------------------------------------------------
  * out[t] = y_sh[t] + sum_{j=0}^{k-1} topk_w[t][j] * y_perm[dest[t*k+j]]

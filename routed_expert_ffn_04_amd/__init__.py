@@ -31,8 +31,8 @@ SCORE = {"softmax": SOFTMAX, "sigmoid": SIGMOID}
 EXPORTS = [
     "moe_route", "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
     "moe_quant_e4m3_1x128", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
-    "moe_combine", "moe_layer", "moe_layer_workspace_size", "moe_layer_noalloc", "moe_status_string",
-    "moe_last_error",
+    "moe_combine", "moe_layer", "moe_layer_workspace_size", "moe_layer_noalloc", "moe_mx_pack_scales",
+    "moe_status_string", "moe_last_error",
 ]
 
 
@@ -45,7 +45,8 @@ class MoeError(RuntimeError):
 class ExpertsT(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("dt", ctypes.c_int32),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("s_gate_up_packed", ctypes.c_void_p), ("s_down_packed", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_workspace_size": ([_I32] * 10, _SZ),
             "moe_layer_noalloc": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(ExpertsT),
                                    ctypes.POINTER(ExpertsT), _P, _I32, _I32, _P, _P, _P, _P], _I32),
+            "moe_mx_pack_scales": ([ctypes.POINTER(ExpertsT), _P, _P, _P], _I32),
             "moe_status_string": ([_I32], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -135,6 +137,8 @@ class Experts:
     s_up: object = None
     s_down: object = None
     dt: Optional[int] = None
+    s_gate_up_packed: object = None    # MXFP4: exponents in the 16-row tiles' order (pack_mx_scales)
+    s_down_packed: object = None
 
     def struct(self) -> ExpertsT:
         n, I, H = self.w_gate.shape
@@ -144,12 +148,32 @@ class Experts:
         for t in (self.w_gate, self.w_up, self.w_down):
             assert t.is_contiguous() and t.is_cuda
         return ExpertsT(n, H, I, dt, _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down),
-                        _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down))
+                        _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down),
+                        _ptr(self.s_gate_up_packed), _ptr(self.s_down_packed))
+
+    def pack_mx_scales(self, stream=None) -> "Experts":
+        """A copy of this MXFP4 bank that also carries its exponents in the
+        16-row tiles' order (moe_mx_pack_scales): a weight-load-time step.
+        Returns the bank unchanged where the shape does not allow it
+        (H % 1024 or I % 512 nonzero) or the weights are not MXFP4."""
+        import dataclasses
+        import torch
+        st = self.struct()
+        if st.dt != MXFP4 or st.H % 1024 or st.I % 512:
+            return self
+        dev = self.w_gate.device
+        gu = torch.empty(2 * st.n * st.I * (st.H // 32), dtype=torch.uint8, device=dev)
+        dn = torch.empty(st.n * st.H * (st.I // 32), dtype=torch.uint8, device=dev)
+        _check(lib().moe_mx_pack_scales(ctypes.byref(st), _ptr(gu), _ptr(dn), _stream(stream)))
+        return dataclasses.replace(self, s_gate_up_packed=gu, s_down_packed=dn)
 
     @staticmethod
-    def from_bank(bank) -> "Experts":
-        return Experts(bank.w_gate, bank.w_up, bank.w_down, bank.s_gate, bank.s_up, bank.s_down,
-                       MXFP4 if bank.dt == "mxfp4" else None)
+    def from_bank(bank, pack: bool = True) -> "Experts":
+        """Device bank of a synthetic bank; MXFP4 banks also get their packed
+        exponents unless pack is False."""
+        e = Experts(bank.w_gate, bank.w_up, bank.w_down, bank.s_gate, bank.s_up, bank.s_down,
+                    MXFP4 if bank.dt == "mxfp4" else None)
+        return e.pack_mx_scales() if pack and bank.dt == "mxfp4" else e
 
 
 # ---------------------------------------------------------------- entry points

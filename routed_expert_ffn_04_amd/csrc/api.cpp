@@ -46,6 +46,12 @@ moe_status_t check_bank(const moe_experts_t* b, int n, int H, int I, const char*
         return fail(MOE_ERR_INVALID, "%s: E4M3 / MXFP4 bank without scales", name);
     if (b->dt == MOE_MXFP4 && (((uintptr_t)b->s_gate | (uintptr_t)b->s_up | (uintptr_t)b->s_down) & 3u))
         return fail(MOE_ERR_INVALID, "%s: MXFP4 exponents must be 4-byte aligned", name);
+    if ((b->s_gate_up_packed || b->s_down_packed) &&
+        (b->dt != MOE_MXFP4 || H % 1024 != 0 || I % 512 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: packed exponents need MXFP4 weights, H %% 1024 == 0 and I %% 512 == 0",
+                    name);
+    if (!aligned16(b->s_gate_up_packed) || !aligned16(b->s_down_packed))
+        return fail(MOE_ERR_INVALID, "%s: packed exponents must be 16-byte aligned", name);
     return MOE_OK;
 }
 
@@ -55,6 +61,7 @@ moe::Bank to_bank(const moe_experts_t* b) {
     k.wg = b->w_gate; k.wu = b->w_up; k.wd = b->w_down;
     // fp32 block scales (E4M3) or E8M0 exponent bytes (MXFP4), by the bank's dtype
     k.sg = (const float*)b->s_gate; k.su = (const float*)b->s_up; k.sd = (const float*)b->s_down;
+    k.xgu = (const uint8_t*)b->s_gate_up_packed; k.xd = (const uint8_t*)b->s_down_packed;
     return k;
 }
 
@@ -221,6 +228,27 @@ moe_status_t moe_grouped_ffn(const void* a, int32_t a_dt, const void* a_scale, c
     p.H = H; p.I = I; p.y = y; p.y_sh = y_sh; p.y_bf16 = (y_dt == MOE_BF16);
     p.y_e4m3 = (y_dt == MOE_E4M3); p.y_scale = y_scale; p.y_sh_bf16 = (y_sh_dt == MOE_BF16);
     return hip_check(moe::launch_gffn(p, ws, (hipStream_t)stream), "moe_grouped_ffn");
+}
+
+// ------------------------------------------------------------------ packed MXFP4 exponents
+moe_status_t moe_mx_pack_scales(const moe_experts_t* bank, void* s_gate_up_packed, void* s_down_packed,
+                                void* stream) {
+    if (!bank) return fail(MOE_ERR_INVALID, "mx_pack_scales: null bank");
+    if (bank->dt != MOE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "mx_pack_scales: weight dtype %d", bank->dt);
+    const int n = bank->n, H = bank->H, I = bank->I;
+    if (n < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID, "mx_pack_scales: n=%d H=%d I=%d", n, H, I);
+    if (H % 1024 != 0 || I % 512 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "mx_pack_scales: needs H %% 1024 == 0 and I %% 512 == 0 (H=%d I=%d)", H, I);
+    if (s_gate_up_packed && (!bank->s_gate || !bank->s_up))
+        return fail(MOE_ERR_INVALID, "mx_pack_scales: null s_gate / s_up");
+    if (s_down_packed && !bank->s_down) return fail(MOE_ERR_INVALID, "mx_pack_scales: null s_down");
+    if (!aligned16(s_gate_up_packed) || !aligned16(s_down_packed))
+        return fail(MOE_ERR_INVALID, "mx_pack_scales: outputs must be 16-byte aligned");
+    if (n == 0 || (!s_gate_up_packed && !s_down_packed)) return MOE_OK;
+    return hip_check(moe::launch_mx_pack_scales(n, H, I, (const uint8_t*)bank->s_gate, (const uint8_t*)bank->s_up,
+                                                (const uint8_t*)bank->s_down, (uint8_t*)s_gate_up_packed,
+                                                (uint8_t*)s_down_packed, (hipStream_t)stream),
+                     "moe_mx_pack_scales");
 }
 
 // ------------------------------------------------------------------ combine

@@ -88,10 +88,11 @@ __device__ __forceinline__ long act_row(const GArgs& A, const GroupInfo& gi, int
 }  // namespace
 
 // ---------------------------------------------------------------- gate / up
-template <int MB, int KS, int P, int kNB, bool XEX, bool LDSA = false>
+template <int MB, int KS, int P, int kNB, bool XEX, bool LDSA = false, bool XP = false>
 __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     static_assert(!LDSA || (MB == 1 && KS == 1 && !XEX), "activations in LDS: 16-row tiles, all of K per wave, "
                                                          "exponent dwords per step");
+    static_assert(!XP || (LDSA && kNB == 2 && P % 4 == 0), "packed exponents: four weight blocks per wave");
     constexpr int NW = 4 / KS;                 // waves along N
     constexpr int TN = NW * kNB * 16;          // h columns per tile (a multiple of 32)
     constexpr int RS = 2 * TN + 1;
@@ -167,6 +168,11 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
             gep[c] = (const uint8_t*)bk.sg + row * (H / 32) + k0 / 32;
             uep[c] = (const uint8_t*)bk.su + row * (H / 32) + k0 / 32;
         }
+        // XP: the packed exponents of the wave's four weight blocks (gate 0,
+        // gate 1, up 0, up 1), 1 KiB per four steps: one 16-byte load per
+        // lane brings its own bytes of all four blocks
+        const uint8_t* xpp = XP ? bk.xgu + (((size_t)gi.e * (I / 32) + n0 / 32) * (H / 512)) * 1024 + lane * 16 : nullptr;
+        i32x4 xpv[P / 4 > 0 ? P / 4 : 1];
 
         f32x4 accg[MB][kNB], accu[MB][kNB];
 #pragma unroll
@@ -192,6 +198,11 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
             }
         };
         auto load_e = [&](int p, int step) {
+            if constexpr (XP) {
+                // steps step-3 .. step, once step p - 3 .. p of this ring slot group are consumed
+                if ((p & 3) == 3) xpv[p >> 2] = gld<i32x4>(xpp + (size_t)((step - 3) >> 2) * 1024);
+                return;
+            }
 #pragma unroll
             for (int c = 0; c < kNB; ++c) {
                 rge[p][c] = gld<uint32_t>(gep[c] + step * 4);
@@ -249,10 +260,19 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
                     for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
                 }
             } else {
+                if constexpr (XP) {
+                    const uint32_t v = (uint32_t)xpv[p >> 2][p & 3];
 #pragma unroll
-                for (int c = 0; c < kNB; ++c) {
-                    eg[c] = rge[p][c] >> esh;
-                    eu[c] = rue[p][c] >> esh;
+                    for (int c = 0; c < kNB; ++c) {
+                        eg[c] = v >> (8 * c);
+                        eu[c] = v >> (8 * (2 + c));
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < kNB; ++c) {
+                        eg[c] = rge[p][c] >> esh;
+                        eu[c] = rue[p][c] >> esh;
+                    }
                 }
                 if constexpr (!LDSA) {
 #pragma unroll
@@ -357,8 +377,9 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
 }
 
 // ---------------------------------------------------------------- down
-template <int MB, int P, int kNB, bool XEX>
+template <int MB, int P, int kNB, bool XEX, bool XP = false>
 __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
+    static_assert(!XP || (MB == 1 && kNB == 4 && P % 4 == 0 && !XEX), "packed exponents: four weight blocks per wave");
     constexpr int TN = 4 * kNB * 16;           // output (H) columns per tile; each wave all of K
     constexpr int RS = TN + 1;
     const int H = A.H, I = A.I;
@@ -399,6 +420,9 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
             dp[c] = (const uint8_t*)bk.wd + row * (I / 2) + kq * 16;
             dep[c] = (const uint8_t*)bk.sd + row * (I / 32);
         }
+        // XP: the packed exponents of the wave's four weight blocks, 1 KiB per four steps
+        const uint8_t* xpp = XP ? bk.xd + (((size_t)gi.e * (H / 64) + n0 / 64) * (I / 512)) * 1024 + lane * 16 : nullptr;
+        i32x4 xpv[P / 4 > 0 ? P / 4 : 1];
 
         f32x4 acc[MB][kNB];
 #pragma unroll
@@ -418,8 +442,12 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
             for (int i = 0; i < MB; ++i) ra[p][i] = load_act(ap[i] + step * 128);
         };
         auto load_e = [&](int p, int step) {
+            if constexpr (XP) {
+                if ((p & 3) == 3) xpv[p >> 2] = gld<i32x4>(xpp + (size_t)((step - 3) >> 2) * 1024);
+            } else {
 #pragma unroll
-            for (int c = 0; c < kNB; ++c) rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
+                for (int c = 0; c < kNB; ++c) rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
+            }
 #pragma unroll
             for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + step * 4);
         };
@@ -443,6 +471,12 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
                 for (int c = 0; c < kNB; ++c) ed[c] = xlane(src, xcd[c][p & 3]) >> esh;
 #pragma unroll
                 for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
+            } else if constexpr (XP) {
+                const uint32_t v = (uint32_t)xpv[p >> 2][p & 3];
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) ed[c] = v >> (8 * c);
+#pragma unroll
+                for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
             } else {
 #pragma unroll
                 for (int c = 0; c < kNB; ++c) ed[c] = rde[p][c] >> esh;
@@ -555,9 +589,11 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     const size_t alds = (size_t)16 * (A.H + 16) + (size_t)16 * (A.H / 32 + 4);
     if (mb == 1 && alds <= kMxGuLdsMax && A.I % (4 * NB * 16) == 0) {
-        auto k = mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
-        static DeviceCache cache;
-        const int g = per_device(cache, [k] {
+        // packed exponents: both banks carry them, and the ring covers K exactly
+        const bool xp = A.routed.xgu && (A.S == 0 || A.shared.xgu) && A.H % 1024 == 0;
+        auto k = xp ? mx_gateup_kernel<1, 1, kMxGuP, NB, false, true, true> : mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
+        static DeviceCache cache, cache_xp;
+        const int g = per_device(xp ? cache_xp : cache, [k] {
             (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGuLdsMax);
             return device_cu_count();   // one workgroup per CU (LDS)
         });
@@ -577,6 +613,10 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     constexpr int NB = kMxDnNb;
     constexpr bool XE = kMxDnXe;
+    if (mb == 1 && A.routed.xd && (A.S == 0 || A.shared.xd) && A.H % (64 * NB) == 0 && A.I % 512 == 0) {
+        MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, false, true>));
+        return hipGetLastError();
+    }
     if (mb == 1) {
         if (A.H % (64 * NB) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, XE>));
         else MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, 2, XE>));
@@ -586,5 +626,58 @@ hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t
     return hipGetLastError();
 }
 #undef MOE_MX_LAUNCH
+
+// ---------------------------------------------------------------- packed exponents
+// One thread per 16-byte lane record of the packed layouts (include/moe.h,
+// moe_mx_pack_scales): record (e, blk, j, lane), byte q = 4 ss + b.
+__global__ __launch_bounds__(256) void mx_pack_gu_kernel(int n, int H, int I, const uint8_t* __restrict__ sg,
+                                                         const uint8_t* __restrict__ su, uint8_t* __restrict__ out) {
+    const int nj = H / 512, nb = I / 32, KB = H / 32;
+    const long rec = (long)blockIdx.x * 256 + threadIdx.x;
+    if (rec >= (long)n * nb * nj * 64) return;
+    const int lane = (int)(rec % 64);
+    const long t = rec / 64;
+    const int j = (int)(t % nj), blk = (int)(t / nj % nb), e = (int)(t / nj / nb);
+    const int c = lane / 16, r = lane % 16;
+    uint8_t v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int ss = q / 4, b = q % 4;
+        const uint8_t* src = b < 2 ? sg : su;
+        v[q] = src[((size_t)e * I + 32 * blk + 16 * (b & 1) + r) * KB + 4 * (4 * j + ss) + c];
+    }
+    *(i32x4*)(out + rec * 16) = *(const i32x4*)v;
+}
+
+__global__ __launch_bounds__(256) void mx_pack_d_kernel(int n, int H, int I, const uint8_t* __restrict__ sd,
+                                                        uint8_t* __restrict__ out) {
+    const int nj = I / 512, nb = H / 64, KB = I / 32;
+    const long rec = (long)blockIdx.x * 256 + threadIdx.x;
+    if (rec >= (long)n * nb * nj * 64) return;
+    const int lane = (int)(rec % 64);
+    const long t = rec / 64;
+    const int j = (int)(t % nj), blk = (int)(t / nj % nb), e = (int)(t / nj / nb);
+    const int c = lane / 16, r = lane % 16;
+    uint8_t v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int ss = q / 4, b = q % 4;
+        v[q] = sd[((size_t)e * H + 64 * blk + 16 * b + r) * KB + 4 * (4 * j + ss) + c];
+    }
+    *(i32x4*)(out + rec * 16) = *(const i32x4*)v;
+}
+
+hipError_t launch_mx_pack_scales(int n, int H, int I, const uint8_t* sg, const uint8_t* su, const uint8_t* sd,
+                                 uint8_t* xgu, uint8_t* xd, hipStream_t s) {
+    if (xgu) {
+        const long recs = (long)n * (I / 32) * (H / 512) * 64;
+        hipLaunchKernelGGL(mx_pack_gu_kernel, dim3((unsigned)((recs + 255) / 256)), dim3(256), 0, s, n, H, I, sg, su, xgu);
+    }
+    if (xd) {
+        const long recs = (long)n * (H / 64) * (I / 512) * 64;
+        hipLaunchKernelGGL(mx_pack_d_kernel, dim3((unsigned)((recs + 255) / 256)), dim3(256), 0, s, n, H, I, sd, xd);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace moe

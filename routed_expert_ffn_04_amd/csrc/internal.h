@@ -38,6 +38,7 @@ hipError_t launch_combine(const void* y_perm, int y_mode, const float* y_scale, 
 struct Bank {
     const void* wg; const void* wu; const void* wd;
     const float* sg; const float* su; const float* sd;
+    const uint8_t* xgu; const uint8_t* xd;   // MXFP4 exponents in the 16-row tiles' order, or null
 };
 
 struct GffnProblem {
@@ -63,6 +64,9 @@ size_t gffn_ws_bytes(int R_max, int G, int S, int H, int I, int dt);
 // Routed outputs as E4M3 codes (the FP8 combine) are written only by the
 // large e4m3 tiles, which need H % 256 == 0 and 32-bit row offsets.
 bool gffn_e4m3_y_supported(int H, int I, int R_max, int S);
+// MXFP4 exponents into the 16-row streaming tiles' order (see moe_mx_pack_scales).
+hipError_t launch_mx_pack_scales(int n, int H, int I, const uint8_t* sg, const uint8_t* su, const uint8_t* sd,
+                                 uint8_t* xgu, uint8_t* xd, hipStream_t s);
 hipError_t launch_gffn(const GffnProblem& p, void* ws, hipStream_t s);
 
 }  // namespace moe

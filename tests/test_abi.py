@@ -172,3 +172,31 @@ def test_e4m3_outputs_refused_where_the_large_tiles_do_not_run():
     st = L.moe_layer(P, moe.BF16, T, H, P, None, 256, 8, 1, ctypes.byref(eb), None, P, moe.BF16, moe.E4M3,
                      None, None, None, P, 1 << 62, None)
     assert st == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_mx_pack_scales_validation():
+    """moe_mx_pack_scales and banks carrying packed exponents: refused for
+    other weight types, shapes the 16-row tiles' packing does not cover and
+    misaligned buffers, all before any launch (dummy pointers)."""
+    L = moe.lib()
+    m4 = _bank(8, 1024, 512, moe.MXFP4)
+    assert L.moe_mx_pack_scales(None, P, P, None) == moe.MOE_ERR_INVALID
+    assert L.moe_mx_pack_scales(ctypes.byref(_bank(8, 1024, 512, moe.BF16)), P, P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_pack_scales(ctypes.byref(_bank(8, 896, 512, moe.MXFP4)), P, P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_pack_scales(ctypes.byref(_bank(8, 1024, 384, moe.MXFP4)), P, P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_pack_scales(ctypes.byref(m4), P + 4, P, None) == moe.MOE_ERR_INVALID     # 16-byte aligned
+    assert L.moe_mx_pack_scales(ctypes.byref(_bank(8, 1024, 512, moe.MXFP4, scales=False)), P, None,
+                                None) == moe.MOE_ERR_INVALID
+    assert L.moe_mx_pack_scales(ctypes.byref(_bank(0, 1024, 512, moe.MXFP4)), P, P, None) == moe.MOE_OK
+    assert L.moe_mx_pack_scales(ctypes.byref(m4), None, None, None) == moe.MOE_OK               # nothing to write
+
+    def call(bank):
+        return L.moe_grouped_ffn(P, moe.MXFP8, P, P, 2, P, 8, 64, ctypes.byref(bank), None, None, 0, None,
+                                 P, 0, None, None, 0, P, 16, None)
+    packed = moe.ExpertsT(8, 1024, 512, moe.MXFP4, P, P, P, P, P, P, P, P)
+    assert call(packed) == moe.MOE_ERR_WORKSPACE                                  # valid up to the workspace
+    bad = moe.ExpertsT(8, 1024, 512, moe.BF16, P, P, P, None, None, None, P, None)
+    assert L.moe_grouped_ffn(P, moe.BF16, None, P, 2, P, 8, 64, ctypes.byref(bad), None, None, 0, None,
+                             P, 0, None, None, 0, P, 16, None) == moe.MOE_ERR_UNSUPPORTED   # packed needs MXFP4
+    assert call(moe.ExpertsT(8, 1536, 512, moe.MXFP4, P, P, P, P, P, P, P, None)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(moe.ExpertsT(8, 1024, 512, moe.MXFP4, P, P, P, P, P, P, None, P + 8)) == moe.MOE_ERR_INVALID

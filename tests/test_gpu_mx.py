@@ -127,3 +127,90 @@ def test_layer_mxfp4_parity(cfg):
     np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
     check_out(out.float().cpu().numpy(), ref["out"], "layer")
+
+
+# ---------------------------------------------------------------- packed exponents
+
+def _pack_reference(sg, su, sd):
+    """The packed layouts of include/moe.h (moe_mx_pack_scales), written out
+    with numpy from their definition: byte q = 4 ss + b of lane c*16 + r."""
+    n, I, KH = sg.shape
+    H = KH * 32
+    KI = sd.shape[2]
+    gu = np.zeros((n, I // 32, H // 512, 64, 16), np.uint8)
+    dn = np.zeros((n, H // 64, I // 512, 64, 16), np.uint8)
+    for lane in range(64):
+        c, r = lane // 16, lane % 16
+        for q in range(16):
+            ss, b = q // 4, q % 4
+            src = sg if b < 2 else su
+            rows = np.arange(I // 32) * 32 + 16 * (b & 1) + r
+            cols = 4 * (4 * np.arange(H // 512) + ss) + c
+            gu[:, :, :, lane, q] = src[:, rows][:, :, cols]
+            rows = np.arange(H // 64) * 64 + 16 * b + r
+            cols = 4 * (4 * np.arange(I // 512) + ss) + c
+            dn[:, :, :, lane, q] = sd[:, rows][:, :, cols]
+    return gu.reshape(-1), dn.reshape(-1)
+
+
+def test_pack_mx_scales_layout():
+    """The packing kernel against the layout's definition, byte for byte
+    (a non-square bank: H = 2048, I = 1024, three experts)."""
+    wl = synth.make_grouped([3, 1, 2], 0, 2048, 1024, dt="mxfp4", seed=77)
+    bank = wl.routed
+    ex = moe.Experts.from_bank(bank.to(DEV))
+    assert ex.s_gate_up_packed is not None and ex.s_down_packed is not None
+    torch.cuda.synchronize()
+    gu_ref, dn_ref = _pack_reference(bank.s_gate.numpy(), bank.s_up.numpy(), bank.s_down.numpy())
+    np.testing.assert_array_equal(ex.s_gate_up_packed.cpu().numpy(), gu_ref)
+    np.testing.assert_array_equal(ex.s_down_packed.cpu().numpy(), dn_ref)
+
+
+PACKED_CASES = [
+    # 16-row tiles with packed exponents: groups of 1..32 rows, an empty expert, the shared expert
+    ([1, 5, 16, 17, 32, 3, 0, 9], 20, 1024, 512),
+    # a shared group of 100 rows (joins the 16-row tiles: fewer than five groups of 33..256 rows)
+    ([4, 60], 100, 2048, 1024),
+]
+
+
+@pytest.mark.parametrize("gm,sm,H,I", PACKED_CASES)
+def test_grouped_ffn_mxfp4_packed_exponents(gm, sm, H, I):
+    """Banks with packed exponents: outputs within the fp8 tolerance of the
+    oracle and bit-identical to the same banks without them."""
+    print(f"grouped mxfp4 packed gm={gm} sm={sm} H={H} I={I}", flush=True)
+    wl = synth.make_grouped(gm, sm, H, I, dt="mxfp4", seed=sum(gm) + 3 * sm)
+    ref = om.grouped_ffn(wl)
+    R = int(sum(gm))
+    a, a_e = moe.quant_mxfp8(wl.x.to(DEV))
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(gm)]), dtype=torch.int32, device=DEV)
+    outs = []
+    for pack in (True, False):
+        routed = moe.Experts.from_bank(wl.routed.to(DEV), pack=pack)
+        shared = moe.Experts.from_bank(wl.shared.to(DEV), pack=pack)
+        assert (routed.s_gate_up_packed is not None) == pack
+        outs.append(moe.grouped_ffn(a, offs, routed, a_scale=a_e, R_max=R, a_sh=a[R:], a_sh_scale=a_e[R:],
+                                    shared=shared, y_dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    yc = outs[0][0].cpu().numpy()
+    starts = np.concatenate([[0], np.cumsum(gm)])
+    for g in range(len(gm)):
+        if gm[g]:
+            check_out(yc[starts[g]:starts[g + 1]], ref[g][1], f"group {g}")
+    check_out(outs[0][1].cpu().numpy(), ref["shared"][1], "shared")
+
+
+def test_layer_mxfp4_packed_exponents():
+    """The fused layer with packed exponents equals the layer without them."""
+    wl = synth.make_layer(64, 1024, 32, 4, 512, w_dt="mxfp4", seed=99, out_dt="f32", score="sigmoid", shared=True)
+    ref = om.moe_layer(wl)
+    f = lambda t: None if t is None else t.to(DEV)
+    outs = []
+    for pack in (True, False):
+        outs.append(moe.layer(f(wl.x), f(wl.w_router), f(wl.bias), wl.k, wl.score,
+                              moe.Experts.from_bank(wl.routed.to(DEV), pack=pack),
+                              moe.Experts.from_bank(wl.shared.to(DEV), pack=pack), out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    check_out(outs[0].cpu().numpy(), ref["out"], "layer packed")
