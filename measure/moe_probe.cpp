@@ -143,6 +143,16 @@ static BankBuf make_bank(int n, int H, int I, int dt, uint64_t seed) {
     }
     b.d.n = n; b.d.H = H; b.d.I = I; b.d.dt = dt;
     b.d.w_gate = g; b.d.w_up = u; b.d.w_down = w;
+    if (dt == MOE_MXFP4 && H % 1024 == 0 && I % 512 == 0) {
+        // the exponents packed for the 16-row tiles, as the Python banks carry them
+        void* xgu = dalloc(2 * ne / 32);
+        void* xd = dalloc(ne / 32);
+        if (moe_mx_pack_scales(&b.d, xgu, xd, nullptr) != MOE_OK) {
+            std::fprintf(stderr, "moe_mx_pack_scales: %s\n", moe_last_error());
+            std::exit(1);
+        }
+        b.d.s_gate_up_packed = xgu; b.d.s_down_packed = xd;
+    }
     return b;
 }
 
