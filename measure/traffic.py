@@ -55,6 +55,7 @@ def build_probe() -> str:
     return PROBE
 GFFN_KERNELS = ("moe::stream_", "moe::tile_", "moe::mid_kernel", "moe::big_kernel", "moe::mx_", "moe::mxbig_kernel",
                 "moe::gffn_build_lists")
+NOT_GFFN = ("moe::mx_pack_",)   # exponent packing: once per bank at weight-load time, not per call
 XCDS = 8          # MI355X accelerator dies
 NAMES = {
     1: "tiny-fp32-T64-H256-E8-top2",
@@ -151,7 +152,7 @@ def main():
             per = pmc_pass(counter, ["file", d, str(args.calls)], args.work, tag)
             tot = 0.0
             for k, vals in per.items():
-                if not any(s in k for s in GFFN_KERNELS):
+                if not any(s in k for s in GFFN_KERNELS) or any(s in k for s in NOT_GFFN):
                     continue
                 b = sum(vals) / ncalls * cal[counter]["bytes_per_kib"]
                 rec["kernels"].setdefault(k, {})[counter] = round(b)
