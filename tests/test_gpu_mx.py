@@ -214,3 +214,37 @@ def test_layer_mxfp4_packed_exponents():
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
     check_out(outs[0].cpu().numpy(), ref["out"], "layer packed")
+
+
+def test_grouped_ffn_mxfp4_packed_many_tiles():
+    """Packed exponents where each persistent workgroup takes several tiles
+    in a row: bit-identical to the same banks without packed exponents.
+    48 experts of 0..32 rows and a shared group of 100 rows at H = 7168,
+    I = 1024, about 65 m-tiles: ~1800 down and ~520 gate/up tiles.  Random
+    E2M1 bytes and E8M0 exponents 2^-9 .. 2^-1, generated on the device."""
+    n, S, H, I = 48, 100, 7168, 1024
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1234)
+    gm = torch.randint(0, 33, (n,), generator=g, device=DEV).cpu().numpy()
+    gm[5] = 0
+    R = int(gm.sum())
+    print(f"grouped mxfp4 packed many tiles R={R} S={S} H={H} I={I}", flush=True)
+
+    def bank(e):
+        u8 = lambda *s: torch.randint(0, 256, s, generator=g, device=DEV, dtype=torch.uint8)
+        ex = lambda *s: torch.randint(118, 127, s, generator=g, device=DEV, dtype=torch.uint8)
+        return moe.Experts(u8(e, I, H // 2), u8(e, I, H // 2), u8(e, H, I // 2),
+                           ex(e, I, H // 32), ex(e, I, H // 32), ex(e, H, I // 32), moe.MXFP4)
+
+    routed, shared = bank(n), bank(1)
+    x = torch.randn(R + S, H, generator=g, device=DEV).to(torch.bfloat16)
+    a, a_e = moe.quant_mxfp8(x)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(gm)]), dtype=torch.int32, device=DEV)
+    outs = []
+    for r, s in ((routed.pack_mx_scales(), shared.pack_mx_scales()), (routed, shared)):
+        outs.append(moe.grouped_ffn(a, offs, r, a_scale=a_e, R_max=R, a_sh=a[R:], a_sh_scale=a_e[R:],
+                                    shared=s, y_dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert outs[0][0].abs().max().item() > 0 and torch.isfinite(outs[0][0]).all()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
