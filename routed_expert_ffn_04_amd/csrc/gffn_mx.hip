@@ -40,6 +40,13 @@ namespace moe {
 namespace {
 
 
+// A load through the constant address space, for data no kernel of the
+// launch writes: at a wave-uniform address the compiler makes it a scalar load.
+template <class T>
+__device__ __forceinline__ T cld(const void* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
 
 // Loads through global-address-space pointers: every operand lives in device
@@ -376,6 +383,238 @@ __global__ __launch_bounds__(256) void mx_gateup_kernel(GArgs A, TileList L) {
     }
 }
 
+// ---------------------------------------------------------------- gate / up, tiles overlapped
+// Workgroup barrier once this wave's LDS operations have completed, leaving
+// its vector-memory operations in flight (__syncthreads would wait for them).
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // vmcnt 63: no wait; lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The 16-row gate/up tiles of banks with packed exponents (activation rows
+// in LDS, two 16-column blocks of gate and of up per wave, P k-steps of
+// weights in flight), with consecutive tiles of a workgroup overlapped.  The
+// next tile's set-up (tile list, group offsets, its rows' src entries) is
+// done at the start of the current tile; the last P k-steps refill the ring
+// with the next tile's first P, and the next tile's activation rows are
+// loaded into LDS right after the epilogue's first barrier (every wave is
+// past its last multiply then).  A tile thus starts with its rows and first
+// weights in flight since the previous epilogue, where it used to look up
+// its rows, load them, wait for them, and only then start its weight
+// stream.  (Loading the rows' first columns earlier, during the last P
+// k-steps, gains nothing: the compiler cannot count the direct loads of a
+// loop of runtime length, so the next multiply would wait for them.)
+// H / 128 is a multiple of P and at least 2 P.
+template <int P>
+__global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L) {
+    static_assert(P % 4 == 0, "one packed exponent record per four k-steps");
+    constexpr int kNB = 2;
+    constexpr int TN = 4 * kNB * 16;           // h columns per tile
+    constexpr int RS = 2 * TN + 1;
+    const int H = A.H, I = A.I;
+    const int ntn = I / TN;
+    const int nsteps = H / 128;
+
+    __shared__ float red[16][RS];
+    extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
+    const int astride = H + 16, estride = H / 32 + 4;
+    uint8_t* exp_lds = act_lds + 16 * astride;
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    // wave-uniform: the next tile's row lookups are then scalar loads, which
+    // do not wait behind the vector loads in flight
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int kq = lane / 16;
+    const uint32_t esh = 8u * kq;
+
+    struct Tile {
+        GroupInfo gi;
+        int m0, nt0;
+        int nrows;                             // the tile's rows within its group (1 .. 16)
+        const uint8_t *gp[kNB], *up[kNB], *xpp;
+        const uint8_t *arow[4], *erow[4];      // this wave's four activation rows and their exponents
+    };
+    // The next tile's set-up runs with the current tile's loads in flight.
+    // Its lookups (tile list, group offsets, src rows: written by earlier
+    // kernels, only read here) go through the constant address space, so
+    // that at wave-uniform addresses they are scalar loads: a vector load
+    // there would make the wave wait for every load issued before it.
+    auto setup = [&](long t, Tile& q) {
+        const int cnt = cld<int>(L.count);
+        const int* ent = (const int*)(L.entries + t % cnt);   // n-major order, as tile_coords<true>
+        const int2 tl = make_int2(cld<int>(ent), cld<int>(ent + 1));
+        const int g = tl.x;
+        if (g < A.G) {
+            q.gi.p0 = min(max(cld<int>(A.offsets + g), 0), A.R_max);
+            q.gi.m = min(max(cld<int>(A.offsets + g + 1) - q.gi.p0, 0), A.R_max - q.gi.p0);
+            q.gi.e = g;
+            q.gi.shared = 0;
+        } else {
+            q.gi.p0 = 0;
+            q.gi.m = A.S;
+            q.gi.e = 0;
+            q.gi.shared = 1;
+        }
+        q.m0 = tl.y;
+        q.nrows = min(16, q.gi.m - q.m0);
+        q.nt0 = (int)(t / cnt) * TN;
+        const int n0 = q.nt0 + wave * kNB * 16;
+        const Bank bk = q.gi.shared ? A.shared : A.routed;
+        const uint8_t* abase = q.gi.shared ? A.a_sh : A.a;
+        const uint8_t* aebase = (const uint8_t*)(q.gi.shared ? A.a_sh_scale : A.a_scale);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = min(q.m0 + 4 * wave + rr, q.gi.m - 1);
+            const long ar = q.gi.shared ? r : A.src ? cld<int>(A.src + q.gi.p0 + r) / A.src_div : q.gi.p0 + r;
+            q.arow[rr] = abase + (size_t)ar * H;
+            q.erow[rr] = aebase + (size_t)ar * (H / 32);
+        }
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            const size_t row = (size_t)q.gi.e * I + n0 + c * 16 + lane % 16;
+            q.gp[c] = (const uint8_t*)bk.wg + row * (H / 2) + kq * 16;
+            q.up[c] = (const uint8_t*)bk.wu + row * (H / 2) + kq * 16;
+        }
+        q.xpp = bk.xgu + (((size_t)q.gi.e * (I / 32) + n0 / 32) * (H / 512)) * 1024 + lane * 16;
+    };
+    // activation columns [k0, k1) and their exponents of this wave's rows, by
+    // direct loads (kept behind the refill loads, which the last multiplies
+    // wait for).  Only the tile's rows within its group are loaded: the
+    // multiplies read row min(r, nrows - 1) for the rows past it, whose
+    // outputs are never stored (a decode tile holds a few rows of 16).
+    auto load_rows = [&](const Tile& q, int k0, int k1) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * wave + rr;
+            if (row >= q.nrows) break;
+            uint8_t* dst = act_lds + row * astride;
+            for (int c = k0; c < k1; c += 1024)
+                if (c + lane * 16 < k1)
+                    __builtin_amdgcn_global_load_lds((const void*)(q.arow[rr] + c + lane * 16),
+                                                     (__attribute__((address_space(3))) void*)(dst + c), 16, 0, 0);
+            uint8_t* edst = exp_lds + row * estride;
+            for (int c = k0 / 32; c < k1 / 32; c += 256)
+                if (c + lane * 4 < k1 / 32)
+                    __builtin_amdgcn_global_load_lds((const void*)(q.erow[rr] + c + lane * 4),
+                                                     (__attribute__((address_space(3))) void*)(edst + c), 4, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    i32x4 rg[P][kNB], ru[P][kNB];
+    i32x4 xpv[P / 4];
+    f32x4 accg[kNB], accu[kNB];
+    auto load = [&](int p, int step, const Tile& q) {
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            rg[p][c] = gld<i32x4>(q.gp[c] + step * 64);
+            ru[p][c] = gld<i32x4>(q.up[c] + step * 64);
+        }
+        // the record of steps step-3 .. step, once slots p-3 .. p have been consumed
+        if ((p & 3) == 3) xpv[p >> 2] = gld<i32x4>(q.xpp + (size_t)((step - 3) >> 2) * 1024);
+    };
+    int arow_lds = 0;                          // this lane's LDS row: min(lane % 16, nrows - 1)
+    auto mma = [&](int p, int step) {
+        const uint8_t* qa = act_lds + arow_lds * astride + step * 128 + kq * 16;
+        const i32x4 lo = *(const i32x4*)qa, hi = *(const i32x4*)(qa + 64);
+        const i32x8 av = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const uint32_t ea = *(const uint32_t*)(exp_lds + arow_lds * estride + step * 4) >> esh;
+        const uint32_t v = (uint32_t)xpv[p >> 2][p & 3];
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            accg[c] = mma_f8f4(av, rg[p][c], accg[c], ea, v >> (8 * c));
+            accu[c] = mma_f8f4(av, ru[p][c], accu[c], ea, v >> (8 * (2 + c)));
+        }
+    };
+
+    TileIter it(L, ntn);
+    if (!it.valid()) return;
+    Tile cur;
+    setup(it.t, cur);
+    load_rows(cur, 0, H);
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(p, p, cur);
+    wait_vm<0>();
+    barrier_lds();
+    for (;;) {
+        arow_lds = min(lane % 16, cur.nrows - 1);
+        it.next();
+        const bool more = it.valid();
+        // the workgroup's last tile overlaps with a copy of itself: its own
+        // rows, and its last P k-steps again (just read, from L2)
+        Tile nx = cur;
+        if (more) setup(it.t, nx);
+        const int nstep0 = more ? 0 : nsteps - P;
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) accg[c] = accu[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < nsteps - P; s0 += P) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                mma(p, s0 + p);
+                load(p, s0 + P + p, cur);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            mma(p, nsteps - P + p);
+            load(p, nstep0 + p, nx);
+        }
+
+        // partial sums -> LDS; row = 4*(lane/16) + q, col = wave*32 + c*16 + lane%16
+#pragma unroll
+        for (int c = 0; c < kNB; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = wave * kNB * 16 + c * 16 + lane % 16;
+                red[4 * kq + q][col] = accg[c][q];
+                red[4 * kq + q][TN + col] = accu[c][q];
+            }
+        barrier_lds();   // also: every wave is past its last multiply
+        load_rows(nx, 0, H);
+        // SwiGLU, then MXFP8 along I (as in mx_gateup_kernel)
+        constexpr int TQ = TN / 4;
+        uint8_t* he = (uint8_t*)A.h_scale;
+        const GroupInfo& gi = cur.gi;
+        for (int e = tid; e < 16 * TQ; e += 256) {
+            const int row = e / TQ, c4 = (e % TQ) * 4;
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float g = 0.f, u = 0.f;   // summed from zero as in mx_gateup_kernel (a -0 sum reads +0)
+                g += red[row][c4 + j];
+                u += red[row][TN + c4 + j];
+                hv[j] = silu_mul(g, u);
+            }
+            float amax = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+            const uint32_t E = mx_e8m0_for_e4m3(amax);
+            const float f = mx_inv_scale(E);
+            const uint32_t code = f32x4_to_e4m3x4(hv[0] * f, hv[1] * f, hv[2] * f, hv[3] * f);
+            const int r = cur.m0 + row;
+            if (r < gi.m) {
+                const int hr = h_row(A, gi, r);
+                *(uint32_t*)(A.h + (size_t)hr * I + cur.nt0 + c4) = code;
+                if ((c4 & 31) == 0) he[(size_t)hr * (I / 32) + (cur.nt0 + c4) / 32] = (uint8_t)E;
+            }
+        }
+        if (!more) {
+            wait_vm<0>();   // no direct load into LDS outlives the workgroup
+            break;
+        }
+        cur = nx;
+        // this wave's rows of the new tile (and its first P k-steps) are in,
+        // then everyone's; the barrier also orders the epilogue's reads of
+        // `red` before the next tile's writes
+        wait_vm<0>();
+        barrier_lds();
+    }
+}
+
 // ---------------------------------------------------------------- down
 template <int MB, int P, int kNB, bool XEX, bool XP = false>
 __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
@@ -589,11 +828,16 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     const size_t alds = (size_t)16 * (A.H + 16) + (size_t)16 * (A.H / 32 + 4);
     if (mb == 1 && alds <= kMxGuLdsMax && A.I % (4 * NB * 16) == 0) {
-        // packed exponents: both banks carry them, and the ring covers K exactly
+        // packed exponents: both banks carry them, and the ring covers K
+        // exactly; consecutive tiles overlapped where K has at least two rings
         const bool xp = A.routed.xgu && (A.S == 0 || A.shared.xgu) && A.H % 1024 == 0;
-        auto k = xp ? mx_gateup_kernel<1, 1, kMxGuP, NB, false, true, true> : mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
-        static DeviceCache cache, cache_xp;
-        const int g = per_device(xp ? cache_xp : cache, [k] {
+        const bool ovl = xp && nst >= 2 * kMxGuP;
+        static_assert(NB == 2 && 1024 % (128 * kMxGuP) == 0, "overlapped tiles: two blocks per wave, H / 128 a multiple of P");
+        auto k = ovl ? mx_gateup_ovl_kernel<kMxGuP>
+               : xp  ? mx_gateup_kernel<1, 1, kMxGuP, NB, false, true, true>
+                     : mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
+        static DeviceCache cache, cache_xp, cache_ovl;
+        const int g = per_device(ovl ? cache_ovl : xp ? cache_xp : cache, [k] {
             (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGuLdsMax);
             return device_cu_count();   // one workgroup per CU (LDS)
         });
