@@ -507,14 +507,23 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
     i32x4 rg[P][kNB], ru[P][kNB];
     i32x4 xpv[P / 4];
     f32x4 accg[kNB], accu[kNB];
-    auto load = [&](int p, int step, const Tile& q) {
+    // the refill of the whole ring with k-steps step0 .. step0 + P - 1, once
+    // its last multiply is issued: the exponent records first, then the
+    // weights.  Scheduling barriers keep that order and the multiplies
+    // above; with the records last, the compiler hoisted their exponent
+    // shifts to the ring's second multiply, which then waited for every load.
+    auto refill = [&](int step0, const Tile& q) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < kNB; ++c) {
-            rg[p][c] = gld<i32x4>(q.gp[c] + step * 64);
-            ru[p][c] = gld<i32x4>(q.up[c] + step * 64);
-        }
-        // the record of steps step-3 .. step, once slots p-3 .. p have been consumed
-        if ((p & 3) == 3) xpv[p >> 2] = gld<i32x4>(q.xpp + (size_t)((step - 3) >> 2) * 1024);
+        for (int g = 0; g < P / 4; ++g) xpv[g] = gld<i32x4>(q.xpp + (size_t)(step0 / 4 + g) * 1024);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                rg[p][c] = gld<i32x4>(q.gp[c] + (step0 + p) * 64);
+                ru[p][c] = gld<i32x4>(q.up[c] + (step0 + p) * 64);
+            }
+        __builtin_amdgcn_sched_barrier(0);
     };
     int arow_lds = 0;                          // this lane's LDS row: min(lane % 16, nrows - 1)
     auto mma = [&](int p, int step) {
@@ -535,8 +544,7 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
     Tile cur;
     setup(it.t, cur);
     load_rows(cur, 0, H);
-#pragma unroll
-    for (int p = 0; p < P; ++p) load(p, p, cur);
+    refill(0, cur);
     wait_vm<0>();
     barrier_lds();
     for (;;) {
@@ -552,16 +560,12 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
         for (int c = 0; c < kNB; ++c) accg[c] = accu[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < nsteps - P; s0 += P) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                mma(p, s0 + p);
-                load(p, s0 + P + p, cur);
-            }
+            for (int p = 0; p < P; ++p) mma(p, s0 + p);
+            refill(s0 + P, cur);
         }
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            mma(p, nsteps - P + p);
-            load(p, nstep0 + p, nx);
-        }
+        for (int p = 0; p < P; ++p) mma(p, nsteps - P + p);
+        refill(nstep0, nx);
 
         // partial sums -> LDS; row = 4*(lane/16) + q, col = wave*32 + c*16 + lane%16
 #pragma unroll
