@@ -621,8 +621,8 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
 
 // ---------------------------------------------------------------- down
 template <int MB, int P, int kNB, bool XEX, bool XP = false>
-__global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
-    static_assert(!XP || (MB == 1 && kNB == 4 && P % 4 == 0 && !XEX), "packed exponents: four weight blocks per wave");
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mx_down_kernel(GArgs A, TileList L) {
+    static_assert(!XP || (MB == 1 && kNB % 4 == 0 && P % 4 == 0 && !XEX), "packed exponents: weight blocks in fours");
     constexpr int TN = 4 * kNB * 16;           // output (H) columns per tile; each wave all of K
     constexpr int RS = TN + 1;
     const int H = A.H, I = A.I;
@@ -663,9 +663,10 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
             dp[c] = (const uint8_t*)bk.wd + row * (I / 2) + kq * 16;
             dep[c] = (const uint8_t*)bk.sd + row * (I / 32);
         }
-        // XP: the packed exponents of the wave's four weight blocks, 1 KiB per four steps
+        // XP: the packed exponents of the wave's weight blocks, 1 KiB per four
+        // blocks (64 rows) and four steps
         const uint8_t* xpp = XP ? bk.xd + (((size_t)gi.e * (H / 64) + n0 / 64) * (I / 512)) * 1024 + lane * 16 : nullptr;
-        i32x4 xpv[P / 4 > 0 ? P / 4 : 1];
+        i32x4 xpv[P / 4 > 0 ? P / 4 : 1][kNB / 4 > 0 ? kNB / 4 : 1];
 
         f32x4 acc[MB][kNB];
 #pragma unroll
@@ -686,7 +687,10 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
         };
         auto load_e = [&](int p, int step) {
             if constexpr (XP) {
-                if ((p & 3) == 3) xpv[p >> 2] = gld<i32x4>(xpp + (size_t)((step - 3) >> 2) * 1024);
+                if ((p & 3) == 3)
+#pragma unroll
+                    for (int q = 0; q < kNB / 4; ++q)
+                        xpv[p >> 2][q] = gld<i32x4>(xpp + ((size_t)q * (I / 512) + ((step - 3) >> 2)) * 1024);
             } else {
 #pragma unroll
                 for (int c = 0; c < kNB; ++c) rde[p][c] = gld<uint32_t>(dep[c] + step * 4);
@@ -715,9 +719,8 @@ __global__ __launch_bounds__(256) void mx_down_kernel(GArgs A, TileList L) {
 #pragma unroll
                 for (int i = 0; i < MB; ++i) ea[i] = xlane(src, xca[i][p & 3]) >> esh;
             } else if constexpr (XP) {
-                const uint32_t v = (uint32_t)xpv[p >> 2][p & 3];
 #pragma unroll
-                for (int c = 0; c < kNB; ++c) ed[c] = v >> (8 * c);
+                for (int c = 0; c < kNB; ++c) ed[c] = (uint32_t)xpv[p >> 2][c >> 2][p & 3] >> (8 * (c & 3));
 #pragma unroll
                 for (int i = 0; i < MB; ++i) ea[i] = rae[p][i] >> esh;
             } else {
@@ -812,6 +815,10 @@ static int mx_persistent_grid(K kernel) {
 constexpr int kMxGuKs = 1, kMxGuP = 8, kMxGuNb = 2;
 constexpr bool kMxGuXe = false;
 constexpr int kMxDnP = 4, kMxDnNb = 4;
+// down with packed exponents: eight 16-column blocks per wave (512-column
+// tiles), which doubles the weight bytes in flight per wave and halves the
+// tiles a decode layer starts
+constexpr int kMxDnNbXp = 8;
 // 16-row gate/up tiles stage the tile's activation rows and exponents in LDS
 // where they fit beside the 16 KiB partial-sum table (H up to 8192): decode
 // layer T = 128 gate/up 0.77 -> 0.74 ms.  Exponent dwords per step there: the
@@ -862,7 +869,8 @@ hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t
     constexpr int NB = kMxDnNb;
     constexpr bool XE = kMxDnXe;
     if (mb == 1 && A.routed.xd && (A.S == 0 || A.shared.xd) && A.H % (64 * NB) == 0 && A.I % 512 == 0) {
-        MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, false, true>));
+        if (A.H % (64 * kMxDnNbXp) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, kMxDnNbXp, false, true>));
+        else MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, false, true>));
         return hipGetLastError();
     }
     if (mb == 1) {
