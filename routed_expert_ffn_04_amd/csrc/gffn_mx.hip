@@ -735,7 +735,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                 for (int i = 0; i < MB; ++i) acc[i][c] = mma_f8f4(ra[p][i], rd[p][c], acc[i][c], ea[i], ed[c]);
         };
         const int nmain = XE ? nsteps / 16 * 16 : nsteps / P * P;
-        if (nmain > 0) {
+        if (XP && nmain > 0) {
+            // the refill of the whole ring once its multiplies are issued:
+            // the exponent records first, then each step's weights and
+            // activations (with the records last, the compiler hoists their
+            // shifts to the ring's first multiplies, which then wait for
+            // every load)
+            auto refill = [&](int step0) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < P / 4; ++g)
+#pragma unroll
+                    for (int q = 0; q < kNB / 4; ++q)
+                        xpv[g][q] = gld<i32x4>(xpp + ((size_t)q * (I / 512) + step0 / 4 + g) * 1024);
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    load_w(p, step0 + p);
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) rae[p][i] = gld<uint32_t>(aep[i] + (step0 + p) * 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            refill(0);
+            int s0 = 0;
+            for (; s0 < nmain - P; s0 += P) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) mma(p, s0, false);
+                refill(s0 + P);
+            }
+#pragma unroll
+            for (int p = 0; p < P; ++p) mma(p, s0, false);
+        } else if (nmain > 0) {
             if (XE) {
                 load_x(0, xcd, xca);
                 if (nmain > 16) load_x(1, xnd, xna);
