@@ -407,11 +407,14 @@ __device__ __forceinline__ void barrier_lds() {
 // k-steps, gains nothing: the compiler cannot count the direct loads of a
 // loop of runtime length, so the next multiply would wait for them.)
 // H / 128 is a multiple of P and at least 2 P.
-template <int P>
-__global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L) {
+template <int P, int NWV>
+__global__ __launch_bounds__(64 * NWV) void mx_gateup_ovl_kernel(GArgs A, TileList L) {
     static_assert(P % 4 == 0, "one packed exponent record per four k-steps");
     constexpr int kNB = 2;
-    constexpr int TN = 4 * kNB * 16;           // h columns per tile
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
+    constexpr int NT = 64 * NWV;               // threads
+    constexpr int RW = 16 / NWV;               // activation rows loaded per wave
+    constexpr int TN = NWV * kNB * 16;         // h columns per tile
     constexpr int RS = 2 * TN + 1;
     const int H = A.H, I = A.I;
     const int ntn = I / TN;
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
         int m0, nt0;
         int nrows;                             // the tile's rows within its group (1 .. 16)
         const uint8_t *gp[kNB], *up[kNB], *xpp;
-        const uint8_t *arow[4], *erow[4];      // this wave's four activation rows and their exponents
+        const uint8_t *arow[RW], *erow[RW];    // this wave's activation rows and their exponents
     };
     // The next tile's set-up runs with the current tile's loads in flight.
     // Its lookups (tile list, group offsets, src rows: written by earlier
@@ -465,8 +468,8 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
         const uint8_t* abase = q.gi.shared ? A.a_sh : A.a;
         const uint8_t* aebase = (const uint8_t*)(q.gi.shared ? A.a_sh_scale : A.a_scale);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = min(q.m0 + 4 * wave + rr, q.gi.m - 1);
+        for (int rr = 0; rr < RW; ++rr) {
+            const int r = min(q.m0 + RW * wave + rr, q.gi.m - 1);
             const long ar = q.gi.shared ? r : A.src ? cld<int>(A.src + q.gi.p0 + r) / A.src_div : q.gi.p0 + r;
             q.arow[rr] = abase + (size_t)ar * H;
             q.erow[rr] = aebase + (size_t)ar * (H / 32);
@@ -487,8 +490,8 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
     auto load_rows = [&](const Tile& q, int k0, int k1) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = 4 * wave + rr;
+        for (int rr = 0; rr < RW; ++rr) {
+            const int row = RW * wave + rr;
             if (row >= q.nrows) break;
             uint8_t* dst = act_lds + row * astride;
             for (int c = k0; c < k1; c += 1024)
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(256) void mx_gateup_ovl_kernel(GArgs A, TileList L)
         constexpr int TQ = TN / 4;
         uint8_t* he = (uint8_t*)A.h_scale;
         const GroupInfo& gi = cur.gi;
-        for (int e = tid; e < 16 * TQ; e += 256) {
+        for (int e = tid; e < 16 * TQ; e += NT) {
             const int row = e / TQ, c4 = (e % TQ) * 4;
             float hv[4];
 #pragma unroll
@@ -854,6 +857,10 @@ constexpr int kMxDnNbXp = 8;
 // layer T = 128 gate/up 0.77 -> 0.74 ms.  Exponent dwords per step there: the
 // 16-step exponent blocks were slower (0.85 ms).
 constexpr size_t kMxGuLdsMax = 140 * 1024;
+// waves of the overlapped 16-row gate/up workgroup (one per CU: LDS): eight
+// waves share one copy of the tile's activation rows over 256 h columns and
+// keep twice the weight bytes in flight
+constexpr int kMxGuOvlWaves = 8;
 constexpr bool kMxDnXe = true;
 // 16-row tiles.  gate/up: K split over kMxGuKs waves when the 128-wide
 // k-steps divide evenly, kMxGuNb column blocks per wave when I is a
@@ -872,17 +879,21 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
         // packed exponents: both banks carry them, and the ring covers K
         // exactly; consecutive tiles overlapped where K has at least two rings
         const bool xp = A.routed.xgu && (A.S == 0 || A.shared.xgu) && A.H % 1024 == 0;
-        const bool ovl = xp && nst >= 2 * kMxGuP;
+        // the overlapped kernel's partial-sum table (static LDS) beside the rows
+        constexpr size_t kOvlRed = (size_t)16 * (2 * kMxGuOvlWaves * NB * 16 + 1) * sizeof(float);
+        constexpr size_t kOvlLdsMax = (size_t)160 * 1024 - kOvlRed;
+        const bool ovl = xp && nst >= 2 * kMxGuP && A.I % (kMxGuOvlWaves * NB * 16) == 0 && alds <= kOvlLdsMax;
         static_assert(NB == 2 && 1024 % (128 * kMxGuP) == 0, "overlapped tiles: two blocks per wave, H / 128 a multiple of P");
-        auto k = ovl ? mx_gateup_ovl_kernel<kMxGuP>
+        auto k = ovl ? mx_gateup_ovl_kernel<kMxGuP, kMxGuOvlWaves>
                : xp  ? mx_gateup_kernel<1, 1, kMxGuP, NB, false, true, true>
                      : mx_gateup_kernel<1, 1, kMxGuP, NB, false, true>;
         static DeviceCache cache, cache_xp, cache_ovl;
-        const int g = per_device(ovl ? cache_ovl : xp ? cache_xp : cache, [k] {
-            (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGuLdsMax);
+        const int g = per_device(ovl ? cache_ovl : xp ? cache_xp : cache, [k, ovl] {
+            (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)(ovl ? kOvlLdsMax : kMxGuLdsMax));
             return device_cu_count();   // one workgroup per CU (LDS)
         });
-        hipLaunchKernelGGL(k, dim3(g), dim3(256), alds, s, A, L);
+        hipLaunchKernelGGL(k, dim3(g), dim3(ovl ? 64 * kMxGuOvlWaves : 256), alds, s, A, L);
         return hipGetLastError();
     }
     if (mb == 1) {
