@@ -9,8 +9,12 @@
 // computed with v_mfma_scale_f32_16x16x128_f8f6f4 and one promotion FMA per
 // accumulator and block, as in gffn_big.hip.  "2 in flight" issues the loads
 // two stages ahead (into the buffer being computed: a timing variant whose
-// numbers are not used).  Prints per variant the time per stage and the
-// shader clock over the run (s_memtime against the 100 MHz s_memrealtime).
+// numbers are not used).  "half the A reads" reloads a wave's token-row
+// fragments only every other 16-row block (timing only, its products are not
+// used): the LDS fragment reads of a stage then total 128 KiB instead of 192,
+// as four waves of 128 x 128 would read.  Prints per variant the time per
+// stage and the shader clock over the run (s_memtime against the 100 MHz
+// s_memrealtime).
 //
 // build: hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //          measure/fp8_stage_bound.hip -o measure/fp8_stage_bound
@@ -52,7 +56,7 @@ __global__ void fill(uint8_t* p, size_t n) {
     }
 }
 
-template <bool LOADS, bool COMPUTE, int D>
+template <bool LOADS, bool COMPUTE, int D, bool HALFA = false>
 __global__ __launch_bounds__(512) void k(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, float* out, unsigned long long* clk) {
     const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(512) void k(const uint8_t* __restrict__ A, const ui
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     i32x8 xn = x;
-                    if (i + 1 < 8) xn = frag8(As, wm * 128 + (i + 1) * 16, fl);
+                    if (i + 1 < 8 && (!HALFA || (i & 1))) xn = frag8(As, wm * 128 + (i + 1) * 16, fl);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         T[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], x, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
@@ -137,9 +141,9 @@ __global__ __launch_bounds__(512) void k(const uint8_t* __restrict__ A, const ui
 }
 
 #define CK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { printf("HIP error %s line %d\n", hipGetErrorString(e_), __LINE__); return 1; } } while (0)
-template <bool LOADS, bool COMPUTE, int D = 1>
+template <bool LOADS, bool COMPUTE, int D = 1, bool HALFA = false>
 int run(const char* name, const uint8_t* A, const uint8_t* W, float* out, unsigned long long* clk) {
-    auto f = k<LOADS, COMPUTE, D>;
+    auto f = k<LOADS, COMPUTE, D, HALFA>;
     const int lds = 2 * kStageBytes + 4096 + 8 * 512 * 4;
     CK(hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
     hipEvent_t a, b; CK(hipEventCreate(&a)); CK(hipEventCreate(&b));
@@ -180,6 +184,8 @@ int main() {
         if (run<false, true>("compute only", A, W, out, clk)) return 1;
         if (run<true, true>("loads + compute", A, W, out, clk)) return 1;
         if (run<true, true, 2>("loads + compute, 2 in flight", A, W, out, clk)) return 1;
+        if (run<false, true, 1, true>("compute only, half the A reads", A, W, out, clk)) return 1;
+        if (run<true, true, 1, true>("loads + compute, half the A reads", A, W, out, clk)) return 1;
     }
     return 0;
 }
