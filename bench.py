@@ -14,14 +14,18 @@ twice on torch's current stream, for the same number of steps:
 Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped decode batch
 (T = 128, H = 7168, 256 routed experts + 1 shared, I = 2048, top-8, bf16),
 whose tokens/s is `value` and whose grouped-FFN HBM rate is `roofline`; the
-same run then times the T = 16384 fp8 layer (the metric's MFMA half) and
-reports it under "prefill_T16384" with its own roofline (fp8 MFMA peak).
+same run then times the decode batch with MXFP4 expert weights (in a child
+process, `bench.py --config 2 --mxfp4`), reported under "decode_mxfp4"
+(roofline against HBM), and the T = 16384 fp8 layer
+(the metric's MFMA half) under "prefill_T16384" with its own roofline (fp8
+MFMA peak).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -385,6 +389,8 @@ def main():
                     help="the layer workload with MXFP4 expert weights (MXFP8 activations and h)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the default decode workload, skip the T=16384 fp8 layer timed after it")
+    ap.add_argument("--no-mxfp4-decode", action="store_true",
+                    help="with the default decode workload, skip the same decode layer with MXFP4 weights")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the T=16384 fp8 layer in the default run")
     args = ap.parse_args()
@@ -421,11 +427,31 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle baseline ...")
         res["cpu_baseline"] = cpu_baseline(wl, cid, args.cpu_sample if cid != 4 else 16)
+    if cid == 2 and not args.mxfp4:
+        del wl, runner, m
+        torch.cuda.empty_cache()
+    if cid == 2 and not args.mxfp4 and not args.no_mxfp4_decode:
+        # the same decode batch with MXFP4 expert weights (the FP4 lever), its
+        # own roofline against HBM.  Timed by `bench.py --config 2 --mxfp4` in
+        # a child process: later in the same process, after the bf16 layer,
+        # the same kernels measured 2-3% slower (cause not found), and either
+        # order would charge that to one of the two decode figures.
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", "2", "--mxfp4", "--no-cpu",
+               "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        sys.stderr.write(r.stderr)
+        line = next((ln for ln in r.stdout.splitlines() if ln.startswith("{")), None)
+        if r.returncode != 0 or line is None:
+            raise RuntimeError(f"MXFP4 decode run failed ({r.returncode}): {r.stdout[-2000:]}")
+        q = json.loads(line)
+        res["decode_mxfp4"] = {k: q[k] for k in ("config", "dtype", "value", "unit", "ms_per_step", "roofline",
+                                                 "grouped_ffn", "calls_ms", "timing", "gpu_clock", "steps")}
+        res["decode_mxfp4"]["process"] = "child: " + " ".join(["bench.py"] + cmd[2:])
     if cid == 2 and not args.mxfp4 and not args.no_prefill:
         # the metric's second half: the grouped FFN's MFMA rate on the T = 16384
         # fp8 layer, timed in the same run with its own roofline (fp8 MFMA peak)
-        del wl, runner, m
-        torch.cuda.empty_cache()
         p = measure(5, args.prefill_steps, args.warmup, dev)
         p.pop("wl"), p.pop("runner")
         res["prefill_T16384"] = {k: p[k] for k in ("config", "dtype", "value", "unit", "ms_per_step", "roofline",
