@@ -909,9 +909,9 @@ hipError_t launch_mx_gateup(int mb, const GArgs& A, const TileList& L, hipStream
 hipError_t launch_mx_down(int mb, const GArgs& A, const TileList& L, hipStream_t s) {
     constexpr int NB = kMxDnNb;
     constexpr bool XE = kMxDnXe;
-    if (mb == 1 && A.routed.xd && (A.S == 0 || A.shared.xd) && A.H % (64 * NB) == 0 && A.I % 512 == 0) {
-        if (A.H % (64 * kMxDnNbXp) == 0) MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, kMxDnNbXp, false, true>));
-        else MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, NB, false, true>));
+    // packed exponents (banks packed only with H % 1024 == 0 and I % 512 == 0)
+    if (mb == 1 && A.routed.xd && (A.S == 0 || A.shared.xd) && A.H % (64 * kMxDnNbXp) == 0 && A.I % 512 == 0) {
+        MOE_MX_LAUNCH((mx_down_kernel<1, kMxDnP, kMxDnNbXp, false, true>));
         return hipGetLastError();
     }
     if (mb == 1) {
