@@ -171,6 +171,9 @@ PACKED_CASES = [
     ([1, 5, 16, 17, 32, 3, 0, 9], 20, 1024, 512),
     # a shared group of 100 rows (joins the 16-row tiles: fewer than five groups of 33..256 rows)
     ([4, 60], 100, 2048, 1024),
+    # H = 8192: the tile's activation rows and the partial sums of the eight-wave
+    # gate/up workgroup exceed LDS, so the four-wave kernel takes the tiles
+    ([3, 20, 1], 10, 8192, 512),
 ]
 
 
